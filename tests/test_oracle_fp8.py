@@ -1,0 +1,118 @@
+"""Pins of the oracle's e4m3fn codec and bf16 helpers (CPU only)."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+
+def _anchors():
+    with open(os.path.join(GOLDEN, "e4m3fn_anchors.json")) as f:
+        return json.load(f)
+
+
+def test_definition_anchor_codes():
+    a = _anchors()["definition_anchors"]
+    for code, val in a["codes"].items():
+        got = fp8.E4M3FN_TABLE[int(code, 16)]
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    for code in a["nan_codes"]:
+        assert math.isnan(fp8.E4M3FN_TABLE[int(code, 16)])
+    assert int(np.isnan(fp8.E4M3FN_TABLE).sum()) == 2
+
+
+def test_page_facts():
+    facts = _anchors()["page_facts"]
+    assert np.nanmax(fp8.E4M3FN_TABLE) == facts[0]["value"] == fp8.E4M3FN_MAX
+    # fnuz's 240 is a finite e4m3fn value but not the top of the range here
+    assert facts[3]["fnuz_max"] in fp8.E4M3FN_TABLE and facts[3]["fnuz_max"] < fp8.E4M3FN_MAX
+
+
+def test_bf16_bit_placement_second_derivation():
+    """InfiniCore's bit-placement identity, applied to all 254 finite codes."""
+    factor = _anchors()["page_facts"][1]["bf16_factor_log2"]
+    c = FINITE.astype(np.uint32)
+    bits = (((c & 0x80) << 8) | ((c & 0x7F) << 4)).astype(np.uint16)
+    placed = fp8.bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(placed * 2.0 ** (-factor), fp8.E4M3FN_TABLE[FINITE])
+    np.testing.assert_array_equal(fp8.e4m3fn_by_bf16_bit_placement(FINITE), fp8.E4M3FN_TABLE[FINITE])
+
+
+def test_f16_bit_placement_third_derivation():
+    factor = _anchors()["page_facts"][2]["f16_factor_log2"]
+    c = FINITE.astype(np.uint32)
+    bits = (((c & 0x80) << 8) | ((c & 0x7F) << 7)).astype(np.uint16)
+    placed = bits.view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(placed * 2.0 ** (-factor), fp8.E4M3FN_TABLE[FINITE])
+
+
+def test_decode_matches_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_values_strictly_increase_over_positive_codes():
+    v = fp8.E4M3FN_TABLE[:0x7F]
+    assert np.all(np.diff(v) > 0)
+    np.testing.assert_array_equal(fp8.E4M3FN_TABLE[0x80:0xFF], -v)
+
+
+def test_encode_roundtrip_all_finite_codes():
+    np.testing.assert_array_equal(fp8.encode_e4m3fn(fp8.E4M3FN_TABLE[FINITE]), FINITE)
+
+
+def test_encode_ties_go_to_even_mantissa():
+    v = fp8.E4M3FN_TABLE[:0x7F]
+    mids = (v[:-1] + v[1:]) / 2
+    got = fp8.encode_e4m3fn(mids).astype(np.int64)
+    lo = np.arange(0x7E)
+    expect = np.where(lo % 2 == 0, lo, lo + 1)
+    np.testing.assert_array_equal(got, expect)
+    # just off the midpoint goes to the nearer side
+    np.testing.assert_array_equal(fp8.encode_e4m3fn(np.nextafter(mids, 0)), lo)
+    np.testing.assert_array_equal(fp8.encode_e4m3fn(np.nextafter(mids, 1e9)), lo + 1)
+
+
+def test_encode_saturates_and_keeps_sign():
+    got = fp8.encode_e4m3fn(np.array([448.0, 449.0, 500.0, 1e30, -1e30, -0.0, -1e-9, 1e-9, np.nan]))
+    np.testing.assert_array_equal(got, [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x80, 0x00, 0x7F])
+
+
+def test_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(100000) * 40, rng.standard_normal(10000) * 1e-3,
+                        rng.uniform(-448, 448, 10000)]).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(fp8.encode_e4m3fn(x), ref)
+
+
+def test_bf16_helpers_match_torch():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(50000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1e-40, 3.4e38, np.inf, -np.inf], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(fp8.f32_to_bf16_bits(x), ref)
+    back = torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(fp8.bf16_bits_to_f64(ref), back)
+
+
+@pytest.mark.parametrize("code", [0x01, 0x07, 0x08, 0x38, 0x7E])
+def test_every_e4m3fn_value_is_exact_in_bf16(code):
+    """The bf16-dot path converts cache bytes to bf16; that must be exact."""
+    v = np.float32(fp8.E4M3FN_TABLE[code])
+    assert fp8.bf16_bits_to_f64(fp8.f32_to_bf16_bits(v)) == v
+    allv = fp8.E4M3FN_TABLE[FINITE].astype(np.float32)
+    np.testing.assert_array_equal(fp8.bf16_bits_to_f64(fp8.f32_to_bf16_bits(allv)), allv)
