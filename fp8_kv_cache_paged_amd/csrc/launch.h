@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host layer (host.cpp) and the HIP
+// kernels (mla_decode.hip). Not installed; include/mla_fp8.h is the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Everything a decode launch needs, resolved and validated on the host.
+struct DecodeLaunch {
+  const uint16_t* q;
+  const uint8_t* kv;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* indices;
+  const float* k_scale;
+  const float* v_scale;
+  uint16_t* out;
+  float* lse;
+  float* part_o;    // workspace, splits > 1
+  float* part_lse;  // workspace, splits > 1
+  int32_t batch, s_q, h_q, d_rope;
+  int32_t num_pages, max_pages, topk, causal, dot;
+  int32_t groups;      // batch (dense) or batch * s_q (sparse)
+  int32_t rows;        // query rows sharing one key stream: s_q*h_q (dense) or h_q (sparse)
+  int32_t row_blocks;  // ceil(rows / 32)
+  int32_t splits;
+  float softmax_scale;
+  bool gather_v;       // debug: byte-gather V^T fragments instead of transposed LDS reads
+  bool debug_print;
+};
+
+// Bytes of the partial-output workspace for the given geometry.
+size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks);
+
+hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
+hipError_t launch_combine(const DecodeLaunch& d, hipStream_t stream);
+
+hipError_t launch_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint16_t* out_bf16,
+                                      int32_t n, hipStream_t stream);
+hipError_t launch_debug_quantize_q(const uint16_t* q, int32_t rows, int32_t row_len,
+                                   uint8_t* codes, int32_t* exps, hipStream_t stream);
+hipError_t launch_debug_gather(const uint8_t* kv, const int32_t* block_table,
+                               const int32_t* seq_lens, int32_t batch, int32_t max_pages,
+                               int32_t num_pages, int32_t d_rope, uint8_t* dense_out,
+                               hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+
+}  // namespace mla

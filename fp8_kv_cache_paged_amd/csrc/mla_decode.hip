@@ -1,0 +1,998 @@
+// FP8-KV paged MLA decode for gfx950 (MI355X / CDNA4).
+//
+// What is computed (FlashMLA PR #82 "update fp8 support", description; ROCm/aiter
+// PR #6199, Technical details; InfiniCore PR #1568, Summary, paged attention):
+// for each query row (token i of s_q, head h of h_q) of a sequence, softmax
+// attention over that sequence's cached latent tokens, K = [e4m3fn nope *
+// k_scale, bf16 rope], V = e4m3fn nope * v_scale, dv = 512, with the natural-log
+// log-sum-exp. Split-KV partials are merged by a log-sum-exp combine
+// (InfiniCore PR #1568, split-kv commit).
+//
+// gfx950 design (the pages' Hopper WGMMA/TMA and gfx942 Triton kernels are prior
+// art only):
+//  * One workgroup per (key stream, split, row group). All query rows of a
+//    sequence (s_q * h_q, up to 128 per workgroup) share the key stream, so a
+//    64-key tile is fetched from HBM once and contracted against every row.
+//    Each wave owns 32 query rows.
+//  * Paged gather: a tile is one page (64 rows of 640 B, contiguous in HBM),
+//    moved by 16-byte global->LDS direct loads into a double-buffered LDS tile
+//    while the previous tile computes (the pages' copy/compute pipelining idea,
+//    FlashMLA PR #82, "Fine-grained optimization of the pipeline"). 16-byte
+//    chunks are XOR-swizzled per row so that column reads are bank-conflict free.
+//  * Orientation S^T = K Q^T on 32x32 MFMA: keys are the M dimension and query
+//    rows the N dimension, so every lane holds one query row and 32 of the 64
+//    keys. Row max and row sum are then per-lane plus one exchange with lane
+//    l^32; P^T is packed straight from the accumulators into the B operand of
+//    the P.V MFMA (no shared-memory round trip, which FlashMLA needed for its
+//    rP -> sP -> rP copies).
+//  * O^T = V^T P^T: the V^T operand is read from the same LDS bytes as K with
+//    the gfx950 transposed LDS read (ds_read_b64_tr_b8); V is never fetched
+//    from HBM a second time.
+//  * fp8 dots: Q nope quantized in-kernel per row with a power-of-two scale,
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (OCP e4m3fn) for Q.K_nope and P.V, the
+//    64 rope dims in bf16 (v_mfma_f32_32x32x16_bf16), as FlashMLA keeps rope in
+//    BF16 tiles. P is scaled by 224 before e4m3fn quantization so the softmax
+//    tail does not flush to zero (ROCm/aiter PR #6199, P scale).
+//    bf16 dots: cache bytes converted exactly to bf16, all products bf16 MFMA.
+//  * Keys past a row's visible length are masked by select (never by
+//    arithmetic) and rows past the sequence end are zero-filled in LDS, so
+//    poisoned slack bytes cannot reach the MFMA (the pages' fill_oob_KV, done
+//    per row at load time instead of with a synchronisation per tile).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "launch.h"
+
+namespace mla {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kKeys = 64;          // keys per tile = page_block
+constexpr int kNope = 512;         // fp8 latent dims = dv
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum { DOT_BF16 = 0, DOT_FP8 = 1 };
+
+// ---------------------------------------------------------------------------
+// e4m3fn conversions (hardware OCP fp8 on gfx950)
+
+// 4 packed e4m3fn bytes -> 4 floats (exact).
+__device__ inline void fp8x4_to_f32(int v, float f[4]) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+  f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
+}
+
+// 4 packed e4m3fn bytes -> 4 bf16 in two dwords (exact: every e4m3fn value is a
+// bf16 value, so the high half of the f32 is the bf16).
+__device__ inline i32x2 fp8x4_to_bf16x4(int v) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+  i32x2 r;
+  r.x = __builtin_amdgcn_perm(__builtin_bit_cast(int, lo.y), __builtin_bit_cast(int, lo.x), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__builtin_bit_cast(int, hi.y), __builtin_bit_cast(int, hi.x), 0x07060302u);
+  return r;
+}
+
+// 4 floats -> 4 packed e4m3fn bytes (round to nearest even).
+__device__ inline int f32x4_to_fp8x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
+
+__device__ inline unsigned bf16x2_bits(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (unsigned)__builtin_bit_cast(unsigned short, x) |
+         ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+__device__ inline float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Smallest integer e with amax <= 448 * 2^e (0 for amax == 0). With
+// amax = f * 2^E, f in [0.5, 1) and 448 = 0.875 * 2^9: e = E - 9 if f <= 0.875,
+// else E - 8.
+__device__ inline int q_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  float f = frexpf(amax, &E);
+  return (f > 0.875f) ? E - 8 : E - 9;
+}
+
+// ---------------------------------------------------------------------------
+// LDS layout. Two tile buffers; each holds a nope region [64 rows][512 B] and
+// a rope region [64 rows][128 B]. The nope regions of both buffers come first
+// (0 and 32 KiB), then the rope regions (64 and 72 KiB), which keeps every
+// nope fragment offset inside the 16-bit ds_read immediate.
+//
+// Within a row, 16-byte chunk c is stored at chunk position c ^ (row & 7).
+// Rows are 0 mod 32 banks apart, so without the swizzle the same column of 8
+// rows would hit the same banks; with it, 8 consecutive rows (or any 8 rows
+// with distinct row & 7) spread over all 32 banks. Only the low three bits of
+// the chunk index are permuted, so each fragment read below needs at most four
+// per-lane base addresses plus compile-time offsets.
+
+constexpr int kNopeRegion = kKeys * kNope;          // 32 KiB per buffer
+constexpr int kRopeRegion = kKeys * 128;            // 8 KiB per buffer
+constexpr int kRopeBase = 2 * kNopeRegion;          // rope regions after both nope regions
+
+template <int ROPE>
+struct Tile {
+  static constexpr int lds_bytes = 2 * kNopeRegion + (ROPE > 0 ? 2 * kRopeRegion : 0);
+};
+
+__device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// One 16-byte-per-lane global->LDS direct load: lane l's 16 bytes from `src`
+// land at lds_base + 16 l (lds_base must be wave-uniform).
+__device__ inline void load_lds16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+// Wave index within the workgroup, as a wave-uniform (scalar) value.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+__device__ inline i32x4 lds_ld16(const uint8_t* base, int off) {
+  return *reinterpret_cast<const i32x4*>(base + off);
+}
+
+// Per-lane byte offsets (within a 64-row page) of the 16-byte chunks a lane
+// moves. Nope load j covers rows 2j, 2j+1 (lane l: row 2j + l/32, chunk
+// position l%32); (2j + l/32) & 7 only depends on j & 3, so four offsets serve
+// all 32 loads: off(j) = nope_lane(j & 3) + 2j * RB. Rope load j covers rows
+// 8j .. 8j+7 (row 8j + l/8, position l%8): off(j) = rope_lane + 8j * RB.
+// Wave w issues the contiguous block of loads w*(32/NW) .., so j & 3 is known
+// at compile time.
+template <int ROPE>
+struct LoadOffsets {
+  int n0, n1, n2, n3;
+  int rope_lane;
+  __device__ LoadOffsets(int lane) {
+    constexpr int RB = kNope + 2 * ROPE;
+    const int hi = lane >> 5, p = lane & 31;
+    n0 = hi * RB + ((p ^ (0 + hi)) << 4);
+    n1 = hi * RB + ((p ^ (2 + hi)) << 4);
+    n2 = hi * RB + ((p ^ (4 + hi)) << 4);
+    n3 = hi * RB + ((p ^ (6 + hi)) << 4);
+    const int r8 = lane >> 3, p8 = lane & 7;
+    rope_lane = r8 * RB + kNope + ((p8 ^ r8) << 4);
+  }
+  __device__ int nope_lane(int v) const { return v == 0 ? n0 : v == 1 ? n1 : v == 2 ? n2 : n3; }
+};
+
+// The offsets are recomputed for every tile from a copy of the lane id the
+// compiler cannot see through: otherwise it hoists the 40 per-load addresses
+// (or the offsets) out of the tile loop and spills them.
+template <int ROPE>
+__device__ inline LoadOffsets<ROPE> fresh_offsets(int lane) {
+  asm volatile("" : "+v"(lane));
+  return LoadOffsets<ROPE>(lane);
+}
+
+// Issue the global->LDS copies of one 64-key tile into buffer `bufi`.
+// Dense tiles read one page: `page_base` points at its first row and rows
+// >= `valid` are zero-filled instead of loaded (the page's slack).
+template <int ROPE, int NW>
+__device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* page_base, int valid,
+                                        int lane, int wave) {
+  constexpr int RB = kNope + 2 * ROPE;
+  const LoadOffsets<ROPE> lo = fresh_offsets<ROPE>(lane);
+  constexpr int NJ = 32 / NW, RJ = 8 / NW;
+  uint8_t* nope = lds + bufi * kNopeRegion + wave * NJ * 1024;
+  uint8_t* rope = lds + kRopeBase + bufi * kRopeRegion + wave * RJ * 1024;
+  const uint8_t* nsrc = page_base + wave * NJ * 2 * RB;
+  const uint8_t* rsrc = page_base + wave * RJ * 8 * RB;
+  const int row0 = wave * NJ * 2 + (lane >> 5), rrow0 = wave * RJ * 8 + (lane >> 3);
+  if (valid == kKeys) {
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 3)), nope + jj * 1024);
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int jj = 0; jj < RJ; ++jj)
+        load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane), rope + jj * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      if (row0 + 2 * jj < valid)
+        load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 3)), nope + jj * 1024);
+      else
+        *reinterpret_cast<i32x4*>(nope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+    }
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int jj = 0; jj < RJ; ++jj) {
+        if (rrow0 + 8 * jj < valid)
+          load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane), rope + jj * 1024);
+        else
+          *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+// Sparse tiles gather 64 independent rows: `mine` is the cache row index
+// (page * 64 + slot) that this lane resolved for tile row `lane`, or -1 for a
+// skipped entry (zero-filled).
+template <int ROPE, int NW>
+__device__ inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* kv, int mine,
+                                         int lane, int wave) {
+  constexpr int RB = kNope + 2 * ROPE;
+  const LoadOffsets<ROPE> lo = fresh_offsets<ROPE>(lane);
+  constexpr int NJ = 32 / NW, RJ = 8 / NW;
+  uint8_t* nope = lds + bufi * kNopeRegion + wave * NJ * 1024;
+  uint8_t* rope = lds + kRopeBase + bufi * kRopeRegion + wave * RJ * 1024;
+  const int row0 = wave * NJ * 2 + (lane >> 5), rrow0 = wave * RJ * 8 + (lane >> 3);
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int cr = __shfl(mine, row0 + 2 * jj);
+    if (cr >= 0)
+      load_lds16(kv + (long)cr * RB + (lo.nope_lane(jj & 3) - (lane >> 5) * RB), nope + jj * 1024);
+    else
+      *reinterpret_cast<i32x4*>(nope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+  }
+  if constexpr (ROPE > 0) {
+#pragma unroll
+    for (int jj = 0; jj < RJ; ++jj) {
+      const int cr = __shfl(mine, rrow0 + 8 * jj);
+      if (cr >= 0)
+        load_lds16(kv + (long)cr * RB + (lo.rope_lane - (lane >> 3) * RB), rope + jj * 1024);
+      else
+        *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+__device__ inline void wait_tile_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Fragment bookkeeping for the 32x32 MFMA, lane l = 32*h + n:
+//  * C/D (16 f32): column n, row 8*(r/4) + 4*h + r%4 for register r.
+//  * A/B operands: lane l supplies row (A) / column (B) n and a slice of the
+//    contraction selected by h. Only the pairing of A and B slices matters, so
+//    both operands are always built with the same (h, byte) -> k assignment.
+//
+// S^T = K Q^T: the A operand's row m is loaded from key 32*kb + key_of_row(m)
+// of the tile. The permutation keeps the 8 lanes of every aligned group on 8
+// rows with distinct row & 7 (conflict free), and makes the 16 keys a lane
+// half owns in a 32-key block pair up into 8-key groups that are again
+// distinct mod 8 for the transposed V reads. With m = 8j + 4hh + i:
+// key = 8j + 4*((j + hh) & 1) + i.
+__device__ inline int key_of_row(int m) {
+  const int j = m >> 3, hh = (m >> 2) & 1, i = m & 3;
+  return 8 * j + 4 * ((j + hh) & 1) + i;
+}
+
+// P^T (B operand of O^T = V^T P^T) is packed from S in register order: byte
+// 8u + e of lane half h is S[u/2][8*(u%2) + e], i.e. key
+//     32*(u/2) + key_of_row(8*(2*(u%2) + e/4) + 4h + e%4) = 16u + tr_key(e, h)
+// and the V^T operand must present the same keys.
+__device__ inline int tr_key(int e, int h) {
+  const int jl = e >> 2;  // low bit of j
+  return 8 * jl + 4 * ((jl + h) & 1) + (e & 3);
+}
+
+// V^T bytes for dv block blk (32 dv values) and contraction bytes 8u .. 8u+7:
+// byte e of the result is V[16u + tr_key(e, h)][32*blk + n] (e4m3fn).
+template <bool GATHER>
+__device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u) {
+  const int h = lane >> 5;
+  if constexpr (GATHER) {
+    const int n = lane & 31;
+    const int dv = 32 * blk + n;
+    unsigned w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = 16 * u + tr_key(e, h);
+      const unsigned byte = nope[key * kNope + (swz(key, dv >> 4) << 4) + (dv & 15)];
+      w[e >> 2] |= byte << (8 * (e & 3));
+    }
+    return i32x2{(int)w[0], (int)w[1]};
+  } else {
+    // ds_read_b64_tr_b8: within each group of 8 lanes, lane e supplies the
+    // address of an 8-byte row segment and every lane i of the group receives
+    // byte i of each segment, in lane order. Group G = lane/8 covers dv
+    // 32*blk + 8*(G%4) + (lane%8); lane e of it supplies key 16u + tr_key(e, h).
+    const int G = lane >> 3, e = lane & 7;
+    const int key = 16 * u + tr_key(e, h);
+    const int dv0 = 32 * blk + 8 * (G & 3);
+    const int off = key * kNope + (swz(key, dv0 >> 4) << 4) + (dv0 & 15);
+    typedef int v2i_lds __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i_lds*)(nope + off));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The S^T = K Q^T products accumulate in VGPRs (inline asm with "v" operands),
+// because the O^T accumulator already fills the 256 AGPRs and the softmax
+// reads S with VALU instructions. These MFMAs are invisible to the compiler's
+// hazard recognizer, so the required wait states are inserted here:
+//  * a chain of MFMAs accumulating into the same registers with the same
+//    opcode needs none between them;
+//  * VALU reads of an MFMA result: at most 18 wait states for the 16-pass
+//    32x32 MFMAs; s_nop_result gives 32;
+//  * an MFMA reading (as A, B or C) registers a VALU instruction wrote needs a
+//    few wait states; every asm MFMA that may follow VALU writes starts with
+//    s_nop 4.
+
+__device__ inline void mfma_fp8_32x32x64(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_32x32x16(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_32x32x16_after_valu(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// O^T += V^T P^T with the accumulator pinned to AGPRs ("a" operands).
+__device__ inline void mfma_fp8_32x32x64_acc(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_32x32x16_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void s_nop_result(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
+// acc *= s for an accumulator that lives in AGPRs, done in place with
+// v_accvgpr_read / v_mul / v_accvgpr_write so the compiler never needs the
+// accumulator in VGPRs (a plain `acc *= s` makes it keep copies of all 256
+// accumulator registers in VGPRs across the tile loop). Callers make sure the
+// MFMAs that wrote `acc` have completed, and end with s_nop 4 before the next
+// MFMA reads it.
+__device__ inline void scale_agpr_acc(f32x16& acc, float s) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = acc[e], tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(s));
+    acc[e] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+// Scalar launch parameters (pointers are passed separately as __restrict__
+// kernel arguments, which lets uniform reads of the read-only tables become
+// scalar loads).
+struct KDims {
+  int32_t s_q, h_q, rows, row_blocks, row_groups, groups, splits;
+  int32_t num_pages, max_pages, topk, causal;
+  float sm_log2;  // softmax_scale * log2(e)
+};
+
+#define MLA_KERNEL_PTRS                                                                   \
+  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,                         \
+      const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,      \
+      const int32_t* __restrict__ indices, const float* __restrict__ k_scale,             \
+      const float* __restrict__ v_scale, uint16_t* __restrict__ out, float* __restrict__ lse, \
+      float* __restrict__ part_o, float* __restrict__ part_lse
+
+// Q staging for the fp8-dot path: lane (n, h) quantizes its half of query row
+// n's 512 nope dims. The row's power-of-two exponent needs the amax of both
+// halves (lanes n and n+32). Fragment t (K = 64 dims 64t .. 64t+63) holds dims
+// 64t + 32h + (0..31) in byte order.
+__device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 qn[8], int& e_out) {
+  unsigned raw[8][16];
+  float amax = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const unsigned w = (unsigned)v[d];
+        raw[t][4 * k + d] = w;
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
+      }
+    }
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  const int e = q_exponent(amax);
+  const float inv = ldexpf(1.f, -e);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const unsigned w0 = raw[t][2 * d], w1 = raw[t][2 * d + 1];
+      qn[t][d] = f32x4_to_fp8x4(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
+                                bf16_hi(w1) * inv);
+    }
+  }
+  e_out = e;
+}
+
+// Softmax bookkeeping runs in the log2 domain with a lazily raised running
+// max: the max used for exponentials is only raised when a tile's max exceeds
+// it by more than tau, so the rescale of the 256 accumulator registers is rare.
+// Every p is then at most 2^tau; the fp8 path stores e4m3fn(p * pscale), with
+// 2^tau * pscale = 448 (the format's largest value), which keeps tail
+// probabilities down to about 2^-17 representable.
+template <int DOT> struct Soft;
+template <> struct Soft<1> { static constexpr float tau = 1.f, pscale = 224.f; };
+template <> struct Soft<0> { static constexpr float tau = 8.f, pscale = 1.f; };
+
+template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(1, 1)))
+void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
+  constexpr int D = kNope + ROPE;               // q row length
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes];
+  uint8_t* const lds = lds_;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 31, h = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int rg = bid % a.row_groups;
+  bid /= a.row_groups;
+  const int s = bid % a.splits;
+  const int g = bid / a.splits;
+
+  const int b = SPARSE ? g / a.s_q : g;
+  int sk = seq_lens[b];
+  sk = max(0, min(sk, a.max_pages * kKeys));
+  const int units = SPARSE ? (a.topk + kKeys - 1) / kKeys : (sk + kKeys - 1) / kKeys;
+  const int u0 = (int)((long)s * units / a.splits);
+  const int u1 = (int)((long)(s + 1) * units / a.splits);
+  const int ntiles = u1 - u0;
+
+  const int rb = rg * NW + wave;              // row block of this wave
+  const bool wave_active = rb < a.row_blocks;
+  const int row = rb * 32 + n;
+  const bool row_ok = row < a.rows;
+  int row_len = 0;                            // dense: keys this row may see
+  if constexpr (!SPARSE) {
+    const int i = row / a.h_q;
+    row_len = a.causal ? sk - (a.s_q - 1 - i) : sk;
+    if (!row_ok) row_len = 0;
+  }
+  const long qrow_idx = (long)g * a.rows + row;
+  const uint16_t* qrow = q + qrow_idx * D;
+
+  const int32_t* bt_row = block_table + (long)b * a.max_pages;
+  const int32_t* idx_row = SPARSE ? indices + (long)g * a.topk : nullptr;
+  constexpr long RB = kNope + 2 * ROPE;
+
+  // Cache row (page * 64 + slot) of sparse entry `e`, or -1 when skipped.
+  auto sparse_row = [&](int e) -> int {
+    int cr = -1;
+    if (e < a.topk) {
+      const int j = idx_row[e];
+      if (j >= 0 && j < sk) {
+        const int page = bt_row[j / kKeys];
+        if (page >= 0 && page < a.num_pages) cr = page * kKeys + (j % kKeys);
+      }
+    }
+    return cr;
+  };
+  // Dense: one page per tile; the page id of the tile after next is fetched
+  // one iteration early so its scalar load latency hides behind a tile.
+  auto page_of = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
+  auto issue_dense = [&](int unit, int page, int bufi) {
+    const bool ok = page_valid(page);
+    const int valid = ok ? min(kKeys, sk - unit * kKeys) : 0;
+    issue_dense_tile<ROPE, NW>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, lane, wave);
+  };
+
+  int page_cur = -1, page_next = -1;   // dense
+  int row_cur = -1, row_next = -1;     // sparse: this lane's tile row
+  if (ntiles > 0) {
+    if constexpr (SPARSE) {
+      row_cur = sparse_row(u0 * kKeys + lane);
+      issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
+    } else {
+      page_cur = page_of(u0);
+      issue_dense(u0, page_cur, 0);
+      page_next = page_of(u0 + 1);
+    }
+  }
+
+  // Q fragments (B operand of S^T = K Q^T).
+  i32x8 qn[DOT == DOT_FP8 ? 8 : 1];
+  bf16x8 qb[DOT == DOT_BF16 ? 32 : 1];
+  bf16x8 qr[ROPE > 0 ? 4 : 1];
+  float qk_scale;   // q_scale * k_scale, applied to the nope accumulator
+  {
+    const float ks = *k_scale;
+    if constexpr (DOT == DOT_FP8) {
+      int e;
+      stage_q_fp8(qrow, row_ok && wave_active, h, qn, e);
+      qk_scale = ldexpf(ks, e);
+    } else {
+      qk_scale = ks;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int d0 = 32 * (u >> 1) + 16 * h + 8 * (u & 1);
+        i32x4 v = row_ok ? *reinterpret_cast<const i32x4*>(qrow + d0) : i32x4{0, 0, 0, 0};
+        qb[u] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        i32x4 v = row_ok ? *reinterpret_cast<const i32x4*>(qrow + kNope + 16 * t + 8 * h)
+                         : i32x4{0, 0, 0, 0};
+        qr[t] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+
+  // The K operand's row m = n is tile key krow (+ 32 kb); krow & 7 is fixed
+  // per lane, so chunk positions are the logical chunks XOR krow & 7.
+  const int krow = key_of_row(n);
+
+  f32x16 O[16];
+#pragma unroll
+  for (int blk = 0; blk < 16; ++blk) O[blk] = f32x16{};
+  float m_run = -INFINITY;   // max used for the exponentials (log2 domain)
+  float l_run = 0.f;         // this lane's share of the running sum
+
+  for (int k = 0; k < ntiles; ++k) {
+    wait_tile_and_sync();
+    if constexpr (SPARSE) {
+      if (k + 1 < ntiles) {
+        row_next = sparse_row((u0 + k + 1) * kKeys + lane);
+        issue_sparse_tile<ROPE, NW>(lds, (k + 1) & 1, kv, row_next, lane, wave);
+      }
+    } else {
+      if (k + 1 < ntiles) issue_dense(u0 + k + 1, page_next, (k + 1) & 1);
+    }
+    // A wave whose row block lies past the last row (ragged row counts) runs
+    // the same code on zero queries and only skips the stores: a second loop
+    // path around the accumulators makes the register allocator shuffle them.
+    const int page_after = SPARSE ? -1 : page_of(u0 + k + 2);
+    const uint8_t* nope = lds + (k & 1) * kNopeRegion;
+    const uint8_t* rope = lds + kRopeBase + (k & 1) * kRopeRegion;
+    const int unit = u0 + k;
+
+    // ---- S^T = K Q^T -------------------------------------------------------
+    // Fragments are prefetched one MFMA ahead; the scheduling barriers keep
+    // the compiler from hoisting every fragment load of the tile (which would
+    // need up to 128 extra registers).
+    f32x16 S[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc = f32x16{};
+      const int row_off = (32 * kb + krow) * kNope;
+      if constexpr (DOT == DOT_FP8) {
+        auto kfrag = [&](int t) -> i32x8 {
+          const i32x4 lo = lds_ld16(nope, row_off + (swz(krow, 4 * t + 2 * h) << 4));
+          const i32x4 hi = lds_ld16(nope, row_off + (swz(krow, 4 * t + 2 * h + 1) << 4));
+          return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        };
+        i32x8 nxt = kfrag(0);
+        asm volatile("s_nop 4" ::);   // acc was just zeroed by VALU
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const i32x8 cur = nxt;
+          if (t + 1 < 8) nxt = kfrag(t + 1);
+          mfma_fp8_32x32x64(acc, cur, qn[t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        i32x4 nxt = lds_ld16(nope, row_off + (swz(krow, h) << 4));
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const i32x4 raw = nxt;
+          if (t + 1 < 16) nxt = lds_ld16(nope, row_off + (swz(krow, 2 * (t + 1) + h) << 4));
+          const i32x2 b0 = fp8x4_to_bf16x4(raw.x), b1 = fp8x4_to_bf16x4(raw.y);
+          const i32x2 b2 = fp8x4_to_bf16x4(raw.z), b3 = fp8x4_to_bf16x4(raw.w);
+          const bf16x8 a0 = __builtin_bit_cast(bf16x8, i32x4{b0.x, b0.y, b1.x, b1.y});
+          const bf16x8 a1 = __builtin_bit_cast(bf16x8, i32x4{b2.x, b2.y, b3.x, b3.y});
+          mfma_bf16_32x32x16_after_valu(acc, a0, qb[2 * t]);
+          mfma_bf16_32x32x16_after_valu(acc, a1, qb[2 * t + 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      s_nop_result(acc);
+      acc *= qk_scale;
+      if constexpr (ROPE > 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const i32x4 raw = lds_ld16(rope, (32 * kb + krow) * 128 + (swz(krow, 2 * t + h) << 4));
+          if (t == 0) mfma_bf16_32x32x16_after_valu(acc, __builtin_bit_cast(bf16x8, raw), qr[t]);
+          else mfma_bf16_32x32x16(acc, __builtin_bit_cast(bf16x8, raw), qr[t]);
+        }
+        s_nop_result(acc);
+      }
+      S[kb] = acc;
+    }
+
+    // ---- mask + online softmax (log2 domain) --------------------------------
+    unsigned long long smask = 0;
+    bool page_ok = true;
+    if constexpr (SPARSE) smask = __ballot(row_cur >= 0);
+    else page_ok = page_valid(page_cur);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = r >> 2;
+        const int key = 32 * kb + 8 * j + 4 * ((j + h) & 1) + (r & 3);
+        bool valid;
+        if constexpr (SPARSE) valid = (smask >> key) & 1ull;
+        else valid = page_ok && (unit * kKeys + key < row_len);
+        const float z = valid ? S[kb][r] * a.sm_log2 : -INFINITY;
+        S[kb][r] = z;
+        mx = fmaxf(mx, z);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool raise = mx > m_run + Soft<DOT>::tau;
+    if (__ballot(raise)) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+      l_run *= alpha;
+      if (__ballot(raise && m_run != -INFINITY)) {
+        // The previous tile's P.V MFMAs finished before this tile's S^T
+        // results were read (one in-order MFMA pipeline, s_nop_result).
+#pragma unroll
+        for (int blk = 0; blk < 16; ++blk) scale_agpr_acc(O[blk], alpha);
+        asm volatile("s_nop 4" ::);
+      }
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(S[kb][r] - m_use);
+        S[kb][r] = p;
+        psum += p;
+      }
+    }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T ---------------------------------------------------------
+    if constexpr (DOT == DOT_FP8) {
+      constexpr float ps = Soft<DOT>::pscale;
+      i32x8 pb;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int kb = q >> 2, r0 = 4 * (q & 3);
+        pb[q] = f32x4_to_fp8x4(S[kb][r0] * ps, S[kb][r0 + 1] * ps, S[kb][r0 + 2] * ps, S[kb][r0 + 3] * ps);
+      }
+      auto vfrag = [&](int blk) -> i32x8 {
+        i32x8 av;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i32x2 v = vt_bytes<GATHER_V>(nope, lane, blk, u);
+          av[2 * u] = v.x;
+          av[2 * u + 1] = v.y;
+        }
+        return av;
+      };
+      i32x8 nxt = vfrag(0);
+      asm volatile("s_nop 4" ::);   // pb was just written by VALU
+#pragma unroll
+      for (int blk = 0; blk < 16; ++blk) {
+        const i32x8 cur = nxt;
+        if (blk + 1 < 16) nxt = vfrag(blk + 1);
+        mfma_fp8_32x32x64_acc(O[blk], cur, pb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      bf16x8 pb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kb = u >> 1, r0 = 8 * (u & 1);
+        i32x4 w;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d] = (int)bf16x2_bits(S[kb][r0 + 2 * d], S[kb][r0 + 2 * d + 1]);
+        pb[u] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+      for (int blk = 0; blk < 16; ++blk) {
+        i32x2 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = vt_bytes<GATHER_V>(nope, lane, blk, u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i32x2 lo = fp8x4_to_bf16x4(v[u].x), hi = fp8x4_to_bf16x4(v[u].y);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, i32x4{lo.x, lo.y, hi.x, hi.y});
+          mfma_bf16_32x32x16_acc(O[blk], av, pb[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    page_cur = page_next;
+    page_next = page_after;
+    row_cur = row_next;
+  }
+
+  if (!wave_active) return;
+  // The epilogue reads O with VALU: wait for the last P.V MFMAs.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]), "+a"(O[7]),
+                 "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
+
+  // ---- epilogue -----------------------------------------------------------------
+  // O^T register r of block blk is dv 32*blk + 8*(r/4) + 4*h + r%4 of row n.
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float vs = *v_scale;
+  const bool nonempty = l_tot > 0.f;
+  const float inv = nonempty ? vs / (Soft<DOT>::pscale * l_tot) : 0.f;
+  const float lse2 = nonempty ? m_run + log2f(l_tot) : -INFINITY;
+
+  if (a.splits == 1) {
+    if (!row_ok) return;
+    uint16_t* orow = out + qrow_idx * kNope;
+#pragma unroll
+    for (int blk = 0; blk < 16; ++blk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dv = 32 * blk + 8 * j + 4 * h;
+        uint2 w;
+        w.x = bf16x2_bits(O[blk][4 * j] * inv, O[blk][4 * j + 1] * inv);
+        w.y = bf16x2_bits(O[blk][4 * j + 2] * inv, O[blk][4 * j + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dv) = w;
+      }
+    }
+    if (h == 0) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
+  } else {
+    // partials in the accumulator's own register layout (coalesced 64-byte
+    // stores per lane); the combine kernel reads the same layout.
+    const long frag = ((long)s * a.groups + g) * a.row_blocks + rb;
+    float* po = part_o + frag * (16 * 64 * 16);
+#pragma unroll
+    for (int blk = 0; blk < 16; ++blk) {
+      float4* dst = reinterpret_cast<float4*>(po + (blk * 64 + lane) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dst[j] = make_float4(O[blk][4 * j] * inv, O[blk][4 * j + 1] * inv,
+                             O[blk][4 * j + 2] * inv, O[blk][4 * j + 3] * inv);
+    }
+    if (h == 0) part_lse[frag * 32 + n] = lse2;
+  }
+}
+
+// Split combine (InfiniCore PR #1568, split-kv commit; empty partials carry
+// lse = -inf and weight 0, so an all-empty row gives zeros and lse = -inf).
+// One workgroup per (group, 32-row block); thread (blk, lane) merges the 16
+// accumulator values that lane held for dv block blk in every split.
+__global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims a) {
+  const int g = blockIdx.x / a.row_blocks;
+  const int rb = blockIdx.x % a.row_blocks;
+  for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+    const int blk = idx >> 6, lane = idx & 63;
+    const int n = lane & 31, h = lane >> 5;
+    const int row = rb * 32 + n;
+    if (row >= a.rows) continue;
+    float M = -INFINITY;
+    for (int s = 0; s < a.splits; ++s)
+      M = fmaxf(M, part_lse[(((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n]);
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    float W = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < a.splits; ++s) {
+        const long frag = ((long)s * a.groups + g) * a.row_blocks + rb;
+        const float ls = part_lse[frag * 32 + n];
+        if (ls == -INFINITY) continue;
+        const float w = exp2f(ls - M);
+        W += w;
+        const float4* src = reinterpret_cast<const float4*>(part_o + frag * (16 * 64 * 16) + (blk * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = src[j];
+          acc[4 * j] += w * v.x;
+          acc[4 * j + 1] += w * v.y;
+          acc[4 * j + 2] += w * v.z;
+          acc[4 * j + 3] += w * v.w;
+        }
+      }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    const long qrow_idx = (long)g * a.rows + row;
+    uint16_t* orow = out + qrow_idx * kNope;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dv = 32 * blk + 8 * j + 4 * h;
+      uint2 w;
+      w.x = bf16x2_bits(acc[4 * j] * inv, acc[4 * j + 1] * inv);
+      w.y = bf16x2_bits(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + dv) = w;
+    }
+    if (blk == 0 && h == 0) lse[qrow_idx] = (W > 0.f) ? (M + log2f(W)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Test and measurement kernels (same device routines as the decode).
+
+__global__ void debug_decode_kernel(const uint8_t* codes, float* out_f32, uint16_t* out_bf16, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int base = 4 * i;
+  if (base >= n) return;
+  int v = 0;
+  for (int k = 0; k < 4 && base + k < n; ++k) v |= (int)codes[base + k] << (8 * k);
+  float f[4];
+  fp8x4_to_f32(v, f);
+  const i32x2 bb = fp8x4_to_bf16x4(v);
+  for (int k = 0; k < 4 && base + k < n; ++k) {
+    if (out_f32) out_f32[base + k] = f[k];
+    if (out_bf16) out_bf16[base + k] = (uint16_t)((unsigned)bb[k >> 1] >> (16 * (k & 1)));
+  }
+}
+
+// One wave per 32 rows, the same lane split as the decode kernel.
+__global__ __launch_bounds__(64) void debug_quantize_q_kernel(const uint16_t* q, int rows, int row_len,
+                                                              uint8_t* codes, int32_t* exps) {
+  const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
+  const int row = blockIdx.x * 32 + n;
+  const bool ok = row < rows;
+  i32x8 qn[8];
+  int e;
+  stage_q_fp8(q + (long)(ok ? row : 0) * row_len, ok, h, qn, e);
+  if (!ok) return;
+  for (int t = 0; t < 8; ++t)
+    for (int d = 0; d < 8; ++d)
+      *reinterpret_cast<int*>(codes + (long)row * kNope + 64 * t + 32 * h + 4 * d) = qn[t][d];
+  if (h == 0) exps[row] = e;
+}
+
+// Gather check: one workgroup per (sequence, page unit) runs the decode
+// kernel's tile loader and writes the tile back in logical order.
+template <int ROPE>
+__global__ __launch_bounds__(256) void debug_gather_kernel(const uint8_t* kv, const int32_t* block_table,
+                                                           const int32_t* seq_lens, int max_pages,
+                                                           int num_pages, uint8_t* dense_out) {
+  constexpr int RB = kNope + 2 * ROPE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Tile<ROPE>::lds_bytes];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int b = blockIdx.x / max_pages, unit = blockIdx.x % max_pages;
+  int sk = seq_lens[b];
+  sk = max(0, min(sk, max_pages * kKeys));
+  const int page = block_table[(long)b * max_pages + unit];
+  const bool page_ok = page >= 0 && page < num_pages;
+  const int valid = page_ok ? max(0, min(kKeys, sk - unit * kKeys)) : 0;
+  issue_dense_tile<ROPE, 4>(lds, 0, kv + (long)(page_ok ? page : 0) * kKeys * RB, valid, lane, wave);
+  wait_tile_and_sync();
+  uint8_t* dst = dense_out + ((long)b * max_pages + unit) * kKeys * RB;
+  for (int idx = threadIdx.x; idx < kKeys * (RB / 16); idx += 256) {
+    const int r = idx / (RB / 16), c = idx % (RB / 16);
+    const int off = c < 32 ? r * kNope + (swz(r, c) << 4) : kRopeBase + r * 128 + (swz(r, c - 32) << 4);
+    *reinterpret_cast<i32x4*>(dst + r * RB + c * 16) = lds_ld16(lds, off);
+  }
+}
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* src, long n16, float* sink) {
+  int acc = 0;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long)gridDim.x * 256) {
+    const i32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  acc = __reduce_or_sync(0xffffffffffffffffull, acc);
+  if (threadIdx.x == 0) sink[blockIdx.x] = (float)acc;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+
+size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks) {
+  const size_t frags = (size_t)splits * groups * row_blocks;
+  return frags * (16 * 64 * 16 * sizeof(float)) + frags * 32 * sizeof(float);
+}
+
+// Waves per workgroup: one per 32-row block, up to 4 (1, 2 or 4 so that the
+// tile's load instructions divide evenly among them).
+static int waves_per_group(int row_blocks) { return row_blocks >= 3 ? 4 : row_blocks; }
+
+static KDims make_dims(const DecodeLaunch& d) {
+  KDims a;
+  a.s_q = d.s_q; a.h_q = d.h_q; a.rows = d.rows; a.row_blocks = d.row_blocks;
+  const int nw = waves_per_group(d.row_blocks);
+  a.row_groups = (d.row_blocks + nw - 1) / nw;
+  a.groups = d.groups; a.splits = d.splits;
+  a.num_pages = d.num_pages; a.max_pages = d.max_pages; a.topk = d.topk; a.causal = d.causal;
+  a.sm_log2 = d.softmax_scale * kLog2e;
+  return a;
+}
+
+#define MLA_PTR_ARGS(d) \
+  d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
+
+template <int DOT, int ROPE, bool SPARSE, bool GV>
+static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  const int nw = waves_per_group(d.row_blocks);
+  const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
+  switch (nw) {
+    case 1: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 1, GV>), grid, dim3(64), 0, st, MLA_PTR_ARGS(d), a); break;
+    case 2: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 2, GV>), grid, dim3(128), 0, st, MLA_PTR_ARGS(d), a); break;
+    default: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 4, GV>), grid, dim3(256), 0, st, MLA_PTR_ARGS(d), a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DOT, int ROPE, bool SPARSE>
+static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true>(d, a, st)
+                    : launch_nw<DOT, ROPE, SPARSE, false>(d, a, st);
+}
+
+template <int DOT, int ROPE>
+static hipError_t launch_sp(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  return d.topk > 0 ? launch_gv<DOT, ROPE, true>(d, a, st) : launch_gv<DOT, ROPE, false>(d, a, st);
+}
+
+template <int DOT>
+static hipError_t launch_rope(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  return d.d_rope == 64 ? launch_sp<DOT, 64>(d, a, st) : launch_sp<DOT, 0>(d, a, st);
+}
+
+hipError_t launch_decode(const DecodeLaunch& d, hipStream_t st) {
+  const KDims a = make_dims(d);
+  if (d.debug_print)
+    fprintf(stderr, "[mla_fp8] decode grid=%d (groups=%d splits=%d row_groups=%d) block=%d dot=%s rope=%d sparse=%d\n",
+            a.groups * a.splits * a.row_groups, a.groups, a.splits, a.row_groups,
+            64 * waves_per_group(d.row_blocks), d.dot == DOT_FP8 ? "fp8" : "bf16", d.d_rope,
+            d.topk > 0);
+  return d.dot == DOT_FP8 ? launch_rope<DOT_FP8>(d, a, st) : launch_rope<DOT_BF16>(d, a, st);
+}
+
+hipError_t launch_combine(const DecodeLaunch& d, hipStream_t st) {
+  const KDims a = make_dims(d);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(a.groups * a.row_blocks)), dim3(256), 0, st,
+                     MLA_PTR_ARGS(d), a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint16_t* out_bf16,
+                                      int32_t n, hipStream_t st) {
+  const int threads = (n + 3) / 4;
+  hipLaunchKernelGGL(debug_decode_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     codes, out_f32, out_bf16, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_quantize_q(const uint16_t* q, int32_t rows, int32_t row_len, uint8_t* codes,
+                                   int32_t* exps, hipStream_t st) {
+  hipLaunchKernelGGL(debug_quantize_q_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(64), 0, st, q,
+                     rows, row_len, codes, exps);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_gather(const uint8_t* kv, const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t batch, int32_t max_pages, int32_t num_pages, int32_t d_rope,
+                               uint8_t* dense_out, hipStream_t st) {
+  const dim3 grid((unsigned)(batch * max_pages));
+  if (d_rope == 64)
+    hipLaunchKernelGGL((debug_gather_kernel<64>), grid, dim3(256), 0, st, kv, block_table, seq_lens,
+                       max_pages, num_pages, dense_out);
+  else
+    hipLaunchKernelGGL((debug_gather_kernel<0>), grid, dim3(256), 0, st, kv, block_table, seq_lens,
+                       max_pages, num_pages, dense_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t st) {
+  const long n16 = (long)(bytes / 16);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(4096), dim3(256), 0, st, (const i32x4*)src, n16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace mla

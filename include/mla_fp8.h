@@ -1,0 +1,184 @@
+/*
+ * mla_fp8.h -- C ABI of the MI355X (gfx950) FP8-KV paged MLA decode library.
+ *
+ * The operation (FlashMLA PR #82 "update fp8 support", description and the H800
+ * test report; ROCm/aiter PR #6199, Technical details; InfiniCore PR #1568,
+ * Summary, paged attention bullets): multi-head latent attention decode. For
+ * every query token (s_q of them per sequence, 2 with multi-token prediction)
+ * h_q query heads attend to ONE shared latent KV head (h_kv = 1) per cached
+ * token. A cached token row holds 512 OCP e4m3fn "nope" bytes followed by 64
+ * little-endian bf16 rope values (or no rope). K = [nope * k_scale, rope],
+ * V = nope * v_scale. The output is softmax(scale * Q K^T) V over the 512-wide
+ * latent, plus the natural-log log-sum-exp of the scaled logits. Long key
+ * ranges are cut into splits whose partials are merged by a log-sum-exp
+ * combine (InfiniCore PR #1568, split-kv commit).
+ *
+ * Tensor layouts (all device memory, row-major, caller-owned):
+ *   q            bf16   [batch, s_q, h_q, d_nope + d_rope]
+ *   kv_cache     bytes  [num_pages, page_block, h_kv=1, d_nope + 2*d_rope]
+ *                       page_block must be 64; 16-byte aligned base
+ *   block_table  int32  [batch, max_pages_per_seq]   physical page ids
+ *   seq_lens     int32  [batch]                      cached tokens per sequence
+ *   k_scale      f32[1] device pointer (as the FlashInfer XQA launcher's
+ *   v_scale      f32[1]  kvCacheScale, FlashInfer PR #1769): never read on the host
+ *   indices      int32  [batch, s_q, topk]  sparse variant only: logical token
+ *                       positions; entries < 0 or >= seq_len are skipped
+ *   out          bf16   [batch, s_q, h_q, dv]      (dv = d_nope = 512)
+ *   lse          f32    [batch, s_q, h_q]          natural log; -inf for a row
+ *                                                  with no visible key (out = 0)
+ *   workspace    device scratch of mla_fp8_decode_workspace_size() bytes when
+ *                the resolved split count is > 1 (may be NULL otherwise)
+ *
+ * Semantics not fixed by the source pages, as implemented:
+ *   softmax_scale <= 0 selects 1/sqrt(d_nope + d_rope); causal rows are
+ *   bottom-right aligned (token i of s_q sees keys 0 .. seq_len - s_q + i);
+ *   k_scale scales only the fp8 part of K; sparse rows take no causal mask.
+ *   MLA_DOT_FP8 quantizes each query row's nope part to e4m3fn with its own
+ *   power-of-two scale (the smallest 2^e with amax <= 448 * 2^e) and P to
+ *   e4m3fn after multiplying it by 256; MLA_DOT_BF16 keeps Q in bf16 and
+ *   converts the cache bytes to bf16 exactly.
+ *
+ * Ownership, streams and threads: the library never allocates, frees or
+ * synchronizes device memory. Every kernel is enqueued on the caller's
+ * hip_stream (NULL = the default stream). No mutable global state beyond a
+ * per-device cache of the compute-unit count; calls are thread-safe. Results
+ * are deterministic: the same inputs and split count give bitwise equal
+ * output (no atomics).
+ *
+ * Errors: every entry point returns an int32 status (MLA_OK = 0). All host
+ * checks run before any launch, so a failing call enqueues nothing and writes
+ * nothing. Device-side values (seq_lens, block_table entries, indices,
+ * scales) cannot be checked without a synchronization: the kernels clamp
+ * seq_len to [0, max_pages_per_seq * 64] and skip keys whose page id lies
+ * outside [0, num_pages), which keeps every access in bounds; results for
+ * such inputs are otherwise unspecified, as are non-finite or non-positive
+ * scales.
+ */
+#ifndef MLA_FP8_H
+#define MLA_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_API __attribute__((visibility("default")))
+
+/* status codes */
+#define MLA_OK 0
+#define MLA_ERR_NULL 1         /* a required pointer is NULL (incl. scales with an fp8 cache) */
+#define MLA_ERR_SHAPE 2        /* a size is out of range or inconsistent */
+#define MLA_ERR_DTYPE 3        /* kv_dtype is not a known code */
+#define MLA_ERR_UNSUPPORTED 4  /* a known but unsupported encoding or dimension */
+#define MLA_ERR_WORKSPACE 5    /* workspace missing or too small */
+#define MLA_ERR_ALIGN 6        /* a pointer is not aligned as required */
+#define MLA_ERR_HIP 7          /* the HIP runtime reported an error */
+
+/* kv_dtype codes. Only the OCP e4m3fn encoding (or a uint8 view of it) is
+ * read; the other one-byte encodings are refused rather than misread
+ * (ROCm/aiter PR #6199, the foreign-encoding refusal commit). */
+#define MLA_KV_FP8_E4M3FN 0
+#define MLA_KV_UINT8 1          /* raw bytes, taken to be e4m3fn */
+#define MLA_KV_FP8_E4M3FNUZ 2   /* refused: MLA_ERR_UNSUPPORTED */
+#define MLA_KV_FP8_E5M2 3       /* refused: MLA_ERR_UNSUPPORTED */
+#define MLA_KV_INT8 4           /* refused: MLA_ERR_UNSUPPORTED */
+#define MLA_KV_BF16 5           /* refused: MLA_ERR_UNSUPPORTED */
+
+/* contraction precision */
+#define MLA_DOT_BF16 0
+#define MLA_DOT_FP8 1
+
+#define MLA_MAX_SPLITS 64
+
+/* Host-side description of the tensors. */
+typedef struct mla_params {
+  int32_t batch;              /* sequences, >= 1 */
+  int32_t s_q;                /* query tokens per sequence, 1..16 */
+  int32_t h_q;                /* query heads, 1..1024 */
+  int32_t h_kv;               /* latent KV heads: must be 1 */
+  int32_t d_nope;             /* must be 512 */
+  int32_t d_rope;             /* 64 or 0 */
+  int32_t dv;                 /* must equal d_nope */
+  int32_t page_block;         /* tokens per page: must be 64 */
+  int32_t num_pages;          /* pages in kv_cache, >= 1 */
+  int32_t max_pages_per_seq;  /* block_table row length, >= 1 */
+  int32_t kv_dtype;           /* MLA_KV_* */
+  int32_t causal;             /* 0 or 1 (dense only) */
+  int32_t dot;                /* MLA_DOT_BF16 or MLA_DOT_FP8 */
+  int32_t topk;               /* 0 = dense paged; > 0 = sparse, indices required */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(d_nope + d_rope) */
+} mla_params;
+
+/* Host-only validation of *p (no HIP call). Returns MLA_OK or the first
+ * failing check's code. */
+MLA_API int32_t mla_fp8_validate(const mla_params* p);
+
+/* Split count the decode will use. num_splits > 0 is taken as given (capped
+ * at MLA_MAX_SPLITS); 0 selects the smallest s with groups * s >= cu_count,
+ * capped at 16 and at the number of 64-key units per sequence, where groups is
+ * batch (dense) or batch * s_q (sparse). The environment variable
+ * MLA_FP8_NUM_SPLITS, when set to a positive integer, replaces the automatic
+ * choice. Returns a value >= 1, or a negative status on invalid *p. Host-only. */
+MLA_API int32_t mla_fp8_decode_resolve_splits(const mla_params* p, int32_t num_splits,
+                                              int32_t cu_count);
+
+/* Workspace bytes needed for a resolved split count (0 when splits == 1).
+ * Returns 0 for invalid *p or splits < 1. Host-only. */
+MLA_API size_t mla_fp8_decode_workspace_size(const mla_params* p, int32_t splits);
+
+/* The decode. Enqueues one kernel (splits == 1) or the split kernel and the
+ * combine kernel on hip_stream. num_splits as for resolve_splits, with the
+ * current device's compute-unit count. indices may be NULL unless topk > 0;
+ * workspace may be NULL when the resolved split count is 1. */
+MLA_API int32_t mla_fp8_decode(const mla_params* p, const void* q, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const float* k_scale, const float* v_scale, int32_t num_splits,
+                               void* out, float* lse, const int32_t* indices, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
+/* First stage only (timing and tests): with a resolved split count > 1 it
+ * writes the per-split partials into the workspace and launches no combine;
+ * with 1 split it is the whole decode. Arguments as for mla_fp8_decode. */
+MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, const void* kv_cache,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const float* k_scale, const float* v_scale,
+                                        int32_t num_splits, void* out, float* lse,
+                                        const int32_t* indices, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream);
+
+/* Static description of a status code. Never NULL. */
+MLA_API const char* mla_fp8_status_string(int32_t status);
+
+/* --- test and measurement exports (device pointers, caller's stream) --- */
+
+/* Decodes n e4m3fn bytes with the same device routines the decode kernels
+ * use: to f32 (out_f32, may be NULL) and to bf16 bits (out_bf16, may be NULL). */
+MLA_API int32_t mla_fp8_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32,
+                                            uint16_t* out_bf16, int32_t n, void* hip_stream);
+
+/* Runs the fp8-dot path's query quantization on `rows` bf16 rows of length
+ * row_len (the first 512 entries of each row are quantized): writes 512 codes
+ * per row and the power-of-two exponent e per row (q ~ code * 2^e). */
+MLA_API int32_t mla_fp8_debug_quantize_q(const void* q, int32_t rows, int32_t row_len,
+                                         uint8_t* codes, int32_t* exps, void* hip_stream);
+
+/* Copies, through the decode kernel's paged gather (global -> LDS -> global),
+ * the first seq_len rows of every sequence into dense_out
+ * [batch, max_pages_per_seq * 64, row_bytes]; rows at or past seq_len, and
+ * rows of out-of-range pages, come back as zeros. */
+MLA_API int32_t mla_fp8_debug_gather(const mla_params* p, const void* kv_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     void* dense_out, void* hip_stream);
+
+/* Streams `bytes` (a multiple of 16) of device memory and writes one f32 per
+ * workgroup to sink (>= 65536 floats): an HBM read-bandwidth probe. */
+MLA_API int32_t mla_fp8_bench_stream_read(const void* src, size_t bytes, float* sink,
+                                          void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_FP8_H */

@@ -1,0 +1,91 @@
+"""Shared helpers for the GPU tests: move a workload to the device, run the
+library through its C ABI, and compare with the oracle.
+
+Tolerances (stated by the decode's specification): relative L2 error of `out`
+<= 0.5% with bf16 dots and <= 5% with fp8 dots, over the rows that see at
+least one key; `lse` within 1e-3 absolute on those rows; rows with no visible
+key must give out == 0 exactly and lse == -inf. For fp8 dots the lse is
+compared with the oracle evaluated at the kernel's quantized query Q' (the
+quantization itself is checked bit-exactly elsewhere), and `out` with the
+oracle at the exact bf16 query.
+"""
+
+import functools
+
+import numpy as np
+import torch
+
+import fp8_kv_cache_paged_amd as mla
+from oracle import attn
+
+OUT_TOL = {"bf16": 5e-3, "fp8": 5e-2}
+LSE_TOL = 1e-3
+
+
+def device_inputs(w, device="cuda:0"):
+    t = {
+        "q": torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(device),
+        "kv": torch.from_numpy(w.kv_cache).to(device),
+        "bt": torch.from_numpy(w.block_table).to(device),
+        "sl": torch.from_numpy(w.seq_lens).to(device),
+        "ks": torch.tensor([w.k_scale], dtype=torch.float32, device=device),
+        "vs": torch.tensor([w.v_scale], dtype=torch.float32, device=device),
+        "idx": None if w.indices is None else torch.from_numpy(w.indices).to(device),
+    }
+    return t
+
+
+def run(w, t, dot, num_splits=None, **kw):
+    ns = w.num_splits if num_splits is None else num_splits
+    out, lse = mla.decode(t["q"], t["kv"], t["bt"], t["sl"], t["ks"], t["vs"], num_splits=ns, dot=dot,
+                          causal=w.causal, indices=t["idx"], softmax_scale=w.softmax_scale or 0.0, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle(w, q_prime=False):
+    qo = attn.dequantized_q_nope(w.q_bits, w.d_nope) if q_prime else None
+    return attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
+                           d_nope=w.d_nope, d_rope=w.d_rope, causal=w.causal,
+                           softmax_scale=w.softmax_scale, indices=w.indices, q_nope_override=qo)
+
+
+class OracleCache:
+    """Oracle results per workload (the bf16-q and the Q' variants)."""
+
+    def __init__(self, w):
+        self.w = w
+
+    @functools.cached_property
+    def exact(self):
+        return oracle(self.w, q_prime=False)
+
+    @functools.cached_property
+    def qprime(self):
+        return oracle(self.w, q_prime=True)
+
+
+def compare(out, lse, ref_out, ref_lse, ref_lse_for_lse=None, dot="fp8"):
+    """Returns a dict of error figures and asserts the tolerances."""
+    ref_lse_l = ref_lse if ref_lse_for_lse is None else ref_lse_for_lse
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty), "rows with no visible key must give lse = -inf (and only they)"
+    assert np.all(out[empty] == 0), "rows with no visible key must give out = 0"
+    assert np.all(np.isfinite(out)), "non-finite output"
+    live = ~empty
+    num = np.linalg.norm((out - ref_out)[live])
+    den = np.linalg.norm(ref_out[live])
+    rel = float(num / den) if den > 0 else float(num)
+    dl = float(np.max(np.abs(lse[live] - ref_lse_l[live]))) if live.any() else 0.0
+    res = {"rel_l2": rel, "lse_max_abs": dl}
+    assert rel <= OUT_TOL[dot], f"rel-L2 {rel:.3e} > {OUT_TOL[dot]} ({dot} dots)"
+    assert dl <= LSE_TOL, f"max |dlse| {dl:.3e} > {LSE_TOL}"
+    return res
+
+
+def check(w, oc, dot, num_splits=None, t=None, **kw):
+    t = device_inputs(w) if t is None else t
+    out, lse = run(w, t, dot, num_splits, **kw)
+    ref_o, ref_l = oc.exact
+    lse_ref = oc.qprime[1] if dot == "fp8" else ref_l
+    return compare(out, lse, ref_o, ref_l, lse_ref, dot)

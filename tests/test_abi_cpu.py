@@ -1,0 +1,157 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+its host-side checks return the documented status codes (no GPU needed: every
+call here returns before any HIP launch)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import fp8_kv_cache_paged_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not mla.library_available():
+        import __graft_entry__
+        __graft_entry__.build()
+    return mla.lib()
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mla_fp8.h")).read()
+    return sorted(set(re.findall(r"MLA_API\s+[\w\s\*]+?\b(mla_fp8_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_symbols()
+    assert len(names) == 10
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
+    assert set(names) <= exported
+    assert exported <= set(names), f"undeclared exports: {exported - set(names)}"
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(mla.MlaParams) == 15 * 4
+
+
+def good(**kw):
+    base = dict(batch=2, s_q=2, h_q=64, num_pages=10, max_pages_per_seq=5, kv_dtype=torch.uint8)
+    base.update(kw)
+    return mla.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, mla.MLA_OK),
+    ({"kv_dtype": torch.float8_e4m3fn}, mla.MLA_OK),
+    ({"kv_dtype": torch.float8_e4m3fnuz}, mla.MLA_ERR_UNSUPPORTED),
+    ({"kv_dtype": torch.float8_e5m2}, mla.MLA_ERR_UNSUPPORTED),
+    ({"kv_dtype": torch.int8}, mla.MLA_ERR_UNSUPPORTED),
+    ({"kv_dtype": torch.bfloat16}, mla.MLA_ERR_UNSUPPORTED),
+    ({"kv_dtype": 42}, mla.MLA_ERR_DTYPE),
+    ({"h_kv": 2}, mla.MLA_ERR_UNSUPPORTED),
+    ({"d_nope": 256}, mla.MLA_ERR_UNSUPPORTED),
+    ({"d_rope": 32}, mla.MLA_ERR_UNSUPPORTED),
+    ({"d_rope": 0}, mla.MLA_OK),
+    ({"dv": 256}, mla.MLA_ERR_UNSUPPORTED),
+    ({"page_block": 32}, mla.MLA_ERR_UNSUPPORTED),
+    ({"batch": 0}, mla.MLA_ERR_SHAPE),
+    ({"s_q": 0}, mla.MLA_ERR_SHAPE),
+    ({"s_q": 17}, mla.MLA_ERR_SHAPE),
+    ({"h_q": 0}, mla.MLA_ERR_SHAPE),
+    ({"num_pages": 0}, mla.MLA_ERR_SHAPE),
+    ({"max_pages_per_seq": 0}, mla.MLA_ERR_SHAPE),
+    ({"topk": -1}, mla.MLA_ERR_SHAPE),
+    ({"softmax_scale": float("nan")}, mla.MLA_ERR_SHAPE),
+    ({"softmax_scale": float("inf")}, mla.MLA_ERR_SHAPE),
+    ({"softmax_scale": -1.0}, mla.MLA_OK),
+])
+def test_validation_codes(L, kw, status):
+    assert mla.validate(good(**kw)) == status
+
+
+def test_validate_null_params(L):
+    assert L.mla_fp8_validate(None) == mla.MLA_ERR_NULL
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert mla.status_string(s)
+    assert mla.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("batch,pages,expect", [(64, 129, 4), (32, 129, 8), (128, 129, 2), (256, 129, 1),
+                                                (1, 129, 16), (3, 129, 16), (300, 129, 1), (32, 5, 5),
+                                                (1, 1, 1)])
+def test_auto_splits(L, batch, pages, expect, monkeypatch):
+    # smallest s with batch * s >= 256 CUs, capped at 16 and at the pages per stream
+    monkeypatch.delenv("MLA_FP8_NUM_SPLITS", raising=False)
+    p = good(batch=batch, max_pages_per_seq=pages)
+    assert mla.resolve_splits(p, 0, 256) == expect
+
+
+def test_auto_splits_sparse_counts_tokens_as_groups(L, monkeypatch):
+    monkeypatch.delenv("MLA_FP8_NUM_SPLITS", raising=False)
+    p = good(batch=16, h_q=16, topk=2048, d_rope=0)
+    assert mla.resolve_splits(p, 0, 256) == 8          # 32 (sequence, token) streams
+
+
+def test_explicit_and_env_splits(L, monkeypatch):
+    p = good(max_pages_per_seq=200)
+    assert mla.resolve_splits(p, 3, 256) == 3
+    assert mla.resolve_splits(p, 1000, 256) == mla.MLA_MAX_SPLITS
+    assert mla.resolve_splits(p, -1, 256) < 0
+    monkeypatch.setenv("MLA_FP8_NUM_SPLITS", "7")
+    assert mla.resolve_splits(p, 0, 256) == 7
+    assert mla.resolve_splits(p, 2, 256) == 2
+    assert mla.resolve_splits(good(batch=0), 0, 256) == -mla.MLA_ERR_SHAPE
+
+
+def test_workspace_size(L):
+    p = good(batch=64, s_q=2, h_q=64)
+    assert mla.workspace_size(p, 1) == 0
+    frags = 4 * 64 * 4
+    assert mla.workspace_size(p, 4) == frags * (16 * 64 * 16 * 4 + 32 * 4)
+    assert mla.workspace_size(good(batch=0), 4) == 0
+
+
+def _decode_call(L, p, **ptrs):
+    d = dict(q=16, kv=16, bt=16, sl=16, ks=16, vs=16, out=16, lse=16, idx=None, ws=None)
+    d.update(ptrs)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.mla_fp8_decode(ctypes.byref(p), v(d["q"]), v(d["kv"]), v(d["bt"]), v(d["sl"]), v(d["ks"]),
+                            v(d["vs"]), 1, v(d["out"]), v(d["lse"]), v(d["idx"]), v(d["ws"]), 0, None)
+
+
+def test_decode_rejects_before_any_launch(L):
+    # host pointers that are never dereferenced: every call fails a host check first
+    p = good()
+    assert _decode_call(L, p, q=None) == mla.MLA_ERR_NULL
+    assert _decode_call(L, p, ks=None) == mla.MLA_ERR_NULL      # fp8 cache without scales
+    assert _decode_call(L, p, vs=None) == mla.MLA_ERR_NULL
+    assert _decode_call(L, p, lse=None) == mla.MLA_ERR_NULL
+    assert _decode_call(L, good(topk=8), idx=None) == mla.MLA_ERR_NULL
+    assert _decode_call(L, p, q=24) == mla.MLA_ERR_ALIGN
+    assert _decode_call(L, p, kv=8) == mla.MLA_ERR_ALIGN
+    assert _decode_call(L, p, sl=18) == mla.MLA_ERR_ALIGN
+    assert _decode_call(L, good(kv_dtype=torch.float8_e5m2)) == mla.MLA_ERR_UNSUPPORTED
+    # explicit splits > 1 need a workspace
+    st = L.mla_fp8_decode(ctypes.byref(p), *[ctypes.c_void_p(16)] * 6, 2, ctypes.c_void_p(16),
+                          ctypes.c_void_p(16), None, None, 0, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+
+
+def test_debug_exports_check_arguments(L):
+    assert L.mla_fp8_debug_decode_e4m3fn(None, None, None, 4, None) == mla.MLA_ERR_NULL
+    assert L.mla_fp8_debug_quantize_q(ctypes.c_void_p(16), 1, 100, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                      None) == mla.MLA_ERR_SHAPE
+    assert L.mla_fp8_bench_stream_read(ctypes.c_void_p(16), 17, ctypes.c_void_p(16), None) == mla.MLA_ERR_SHAPE
+    assert L.mla_fp8_debug_gather(ctypes.byref(good(h_kv=3)), None, None, None, None, None) == mla.MLA_ERR_UNSUPPORTED

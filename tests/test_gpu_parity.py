@@ -1,0 +1,122 @@
+"""Parity of the HIP decode with the float64 oracle on seeded inputs.
+
+Small cases span several tiles, ragged tails, several split counts and the
+degenerate cases (empty sequences, causal rows with no key, a sequence of one
+token, ragged head counts). The five workload configurations and the
+benchmark shape then run at their full sizes, in the launch configuration the
+benchmark uses (auto splits), compared element by element with the oracle.
+All slack and unused pages are 0xFF (NaN) bytes, so any stray read of them
+would poison the output and fail the finiteness check.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+_ORACLES = {}
+
+
+def _case(name, **kw):
+    key = (name, tuple(sorted((k, str(v)) for k, v in kw.items())))
+    if key not in _ORACLES:
+        w = workloads.make(name, **kw)
+        _ORACLES[key] = (w, gu.OracleCache(w), gu.device_inputs(w))
+    return _ORACLES[key]
+
+
+SMALL = [
+    ("tiny", {}),
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 64, "seq_len": [300, 1], "seed": 21}),
+    ("tiny", {"batch": 3, "s_q": 2, "h_q": 48, "seq_len": [130, 64, 2], "seed": 22}),   # 96 rows: 3 row blocks
+    ("tiny", {"batch": 2, "s_q": 1, "h_q": 8, "seq_len": [200, 33], "seed": 23}),
+    ("tiny", {"batch": 2, "s_q": 4, "h_q": 64, "seq_len": [700, 3], "seed": 24}),      # 256 rows: 2 row groups
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 16, "d_rope": 0, "seq_len": [257, 90], "seed": 25}),
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 64, "seq_len": [600, 450], "causal": False, "seed": 26}),
+]
+
+
+@pytest.mark.parametrize("dot", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [1, 2, 3, 0])
+@pytest.mark.parametrize("idx", range(len(SMALL)))
+def test_small_dense(idx, splits, dot):
+    name, kw = SMALL[idx]
+    w, oc, t = _case(name, **kw)
+    res = gu.check(w, oc, dot, num_splits=splits, t=t)
+    print(f"{name}{kw} splits={splits} dot={dot}: {res}")
+
+
+@pytest.mark.parametrize("dot", ["bf16", "fp8"])
+def test_empty_and_degenerate_rows(dot):
+    # sequence lengths 0 and 1 with s_q = 2 (causal): whole sequences and single
+    # rows without any visible key
+    w, oc, t = _case("tiny", batch=4, s_q=2, h_q=32, seq_len=[0, 1, 65, 0], seed=31)
+    for splits in (1, 4):
+        gu.check(w, oc, dot, num_splits=splits, t=t)
+    ref_l = oc.exact[1]
+    assert np.isneginf(ref_l[0]).all() and np.isneginf(ref_l[1, 0]).all() and np.isfinite(ref_l[1, 1]).all()
+
+
+@pytest.mark.parametrize("dot", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_small_sparse(dot, splits):
+    w, oc, t = _case("sparse", batch=2, seq_len=5000, topk=300, seed=41)
+    idx = t["idx"].clone()
+    idx[0, 0, 5] = -1
+    idx[1, 1, 17] = 5000       # == seq_len: skipped
+    idx[1, 0, 0] = -7
+    w.indices = idx.cpu().numpy()
+    t = dict(t, idx=idx)
+    oc = gu.OracleCache(w)
+    gu.check(w, oc, dot, num_splits=splits, t=t)
+
+
+def test_more_splits_than_pages_gives_empty_splits():
+    w, oc, t = _case("tiny", batch=2, s_q=2, h_q=64, seq_len=[130, 5], seed=51)
+    for dot in ("bf16", "fp8"):
+        gu.check(w, oc, dot, num_splits=9, t=t)
+
+
+def test_transposed_v_reads_match_byte_gather(monkeypatch):
+    """The V^T operand read with ds_read_b64_tr_b8 equals a plain byte gather."""
+    w, oc, t = _case("tiny", batch=2, s_q=2, h_q=64, seq_len=[300, 77], seed=61)
+    for dot in ("bf16", "fp8"):
+        a = gu.run(w, t, dot, 2)
+        monkeypatch.setenv("MLA_FP8_GATHER_V", "1")
+        b = gu.run(w, t, dot, 2)
+        monkeypatch.delenv("MLA_FP8_GATHER_V")
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_deterministic_repeat():
+    w, oc, t = _case("tiny", batch=2, s_q=2, h_q=64, seq_len=[1000, 333], seed=71)
+    for dot in ("bf16", "fp8"):
+        a = gu.run(w, t, dot, 0)
+        b = gu.run(w, t, dot, 0)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_v_scale_linearity_and_k_scale():
+    w, oc, t = _case("tiny", batch=1, s_q=2, h_q=32, seq_len=[200], seed=81)
+    o1, l1 = gu.run(w, t, "bf16", 1)
+    t2 = dict(t, vs=t["vs"] * 2.0)
+    o2, l2 = gu.run(w, t2, "bf16", 1)
+    assert np.array_equal(l1, l2)
+    np.testing.assert_allclose(o2, 2 * o1, rtol=1e-2, atol=1e-6)
+
+
+# ---- the five configurations and the benchmark shape, full size ----------------
+
+FULL = [("tiny", "bf16"), ("tiny", "fp8"), ("mtp", "bf16"), ("mtp", "fp8"), ("varlen", "fp8"),
+        ("large", "bf16"), ("large", "fp8"), ("sparse", "bf16"), ("sparse", "fp8"), ("metric", "fp8")]
+
+
+@pytest.mark.parametrize("name,dot", FULL)
+def test_full_config(name, dot):
+    w, oc, t = _case(name)
+    res = gu.check(w, oc, dot, t=t)
+    print(f"full {name} dot={dot}: {res}")
