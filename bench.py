@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8-KV paged MLA decode on one MI355X.
+
+Default workload: the benchmark shape b=64, s_q=2 (causal), h_q=64, sk=8196,
+d=576 (512 e4m3fn + 64 bf16 rope), dv=512, 64-token shuffled pages, fp8 dots,
+auto splits. A step is one whole decode call (split kernel + combine) over one
+batch. Calls rotate through enough copies of the KV pool (>= 1 GiB together)
+that the 256 MiB Infinity Cache cannot serve them, so every call reads HBM.
+
+Prints one JSON line: throughput in TFLOP/s (useful FLOPs 2*rows*keys*(576+512)),
+plus ms/call, algorithmic HBM GB/s, a roofline object for the dominant kernel
+(its launches timed with HIP events on the launch stream) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp8_kv_cache_paged_amd as mla  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "FP8-KV MLA decode ms, TFLOPS, HBM GB/s (b=64, s_q=2, sk=8196, h_q=64)"
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="metric", choices=sorted(workloads.SPECS))
+    ap.add_argument("--dot", default="fp8", choices=["fp8", "bf16"])
+    ap.add_argument("--splits", type=int, default=0, help="0 = automatic")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of KV copies to rotate through")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def hbm_read_probe(dev, gib=2.0, reps=5):
+    """Measured HBM read bandwidth (GB/s) of a plain streaming read kernel."""
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(1 << 16, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    mla.stream_read(src, sink)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mla.stream_read(src, sink)
+        e1.record(stream)
+        e1.synchronize()
+        best = max(best, n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src
+    torch.cuda.empty_cache()
+    return best
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (float64 NumPy, unmodified) on a bounded sample of sequences."""
+    from oracle import attn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    flops_done, t_used, seqs = 0.0, 0.0, 0
+    per_seq_flops = []
+    for b in range(w.batch):
+        sub = workloads.Workload(**{**w.__dict__, "batch": 1, "q_bits": w.q_bits[b:b + 1],
+                                    "block_table": w.block_table[b:b + 1], "seq_lens": w.seq_lens[b:b + 1],
+                                    "indices": None if w.indices is None else w.indices[b:b + 1]})
+        t0 = time.perf_counter()
+        attn.mla_decode(sub.q_bits, sub.kv_cache, sub.block_table, sub.seq_lens, sub.k_scale, sub.v_scale,
+                        d_nope=sub.d_nope, d_rope=sub.d_rope, causal=sub.causal, indices=sub.indices,
+                        softmax_scale=sub.softmax_scale)
+        t_used += time.perf_counter() - t0
+        flops_done += workloads.flops(sub)
+        seqs += 1
+        if t_used >= budget_s:
+            break
+    tflops = flops_done / t_used / 1e12
+    sec_per_call = t_used * (workloads.flops(w) / flops_done)
+    return {"value": tflops, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} of {w.batch} sequences of the same workload ({t_used:.1f} s); "
+                      f"scaled: {sec_per_call:.2f} s per full call"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if not mla.library_available():
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = workloads.make(args.workload)
+    flops = workloads.flops(w)
+    nbytes = workloads.algorithmic_bytes(w)
+    print(f"[bench] workload {args.workload}: b={w.batch} s_q={w.s_q} h_q={w.h_q} d_rope={w.d_rope} "
+          f"topk={w.topk} kv={w.kv_cache.nbytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    hbm_meas = hbm_read_probe(dev)
+    print(f"[bench] measured HBM read bandwidth {hbm_meas:.0f} GB/s", file=sys.stderr, flush=True)
+
+    q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    ks = torch.tensor([w.k_scale], dtype=torch.float32, device=dev)
+    vs = torch.tensor([w.v_scale], dtype=torch.float32, device=dev)
+    idx = None if w.indices is None else torch.from_numpy(w.indices).to(dev)
+    kv0 = torch.from_numpy(w.kv_cache).to(dev)
+    copies = max(1, int(np.ceil(args.rotate_bytes * (1 << 30) / kv0.numel())))
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    p = mla.params_for(q, kv0, bt, causal=w.causal, dot=args.dot, indices=idx)
+    splits = args.splits or mla.resolve_splits(p, 0, mla.cu_count(dev))
+    ws_bytes = mla.workspace_size(p, splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    # one call through the binding to validate everything, then the C entry
+    # points directly with prebuilt arguments, so that host overhead stays far
+    # below a kernel's duration and launches queue up back to back
+    mla.decode(q, kv0, bt, sl, ks, vs, num_splits=splits, dot=args.dot, causal=w.causal, indices=idx,
+               out=out, lse=lse, workspace=ws)
+    import ctypes
+    L = mla.lib()
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    argsets = [(ctypes.byref(p), vp(q), vp(kv), vp(bt), vp(sl), vp(ks), vp(vs), splits, vp(out), vp(lse),
+                vp(idx), vp(ws), ws.numel(), st) for kv in kvs]
+
+    def call(i, partials_only=False):
+        fn = L.mla_fp8_decode_partials if partials_only else L.mla_fp8_decode
+        rc = fn(*argsets[i % copies])
+        if rc != 0:
+            raise RuntimeError(f"decode failed: {mla.status_string(rc)}")
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # whole-call timing: K steps between two events, synchronised on both sides
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # the dominant (split) kernel alone, each launch between its own events
+    durs = []
+    for i in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call(i, partials_only=True)
+        b.record(stream)
+        durs.append((a, b))
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+
+    # bytes the split kernel is responsible for: KV rows, Q, tables; out/lse are
+    # written by the combine when splits > 1
+    kern_bytes = nbytes["kv"] + nbytes["q"] + nbytes["tables"] + (0 if splits > 1 else nbytes["out"] + nbytes["lse"])
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if args.dot == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: b={w.batch} s_q={w.s_q} h_q={w.h_q} "
+                               f"sk={int(w.seq_lens.max())} d={w.d_nope + w.d_rope} dv={w.d_nope} "
+                               f"page=64 {'causal' if w.causal else 'non-causal'}"
+                               + (f" topk={w.topk}" if w.topk else ""),
+                   "dots": args.dot, "splits": splits, "kv_copies_rotated": copies},
+        "ms_per_call": round(ms_per_step, 5),
+        "hbm_gbps": round(gbps, 1),
+        "hbm_measured_gbps": round(hbm_meas, 1),
+        "frac_of_measured_hbm": round(gbps / hbm_meas, 4),
+        "frac_of_fp8_mfma_peak": round(tflops / (FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS), 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "mla_decode_kernel", "kernel_us": round(kern_ms * 1e3, 2),
+                     "bytes_per_launch": kern_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,6 +54,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKeys = 64;          // keys per tile = page_block
 constexpr int kNope = 512;         // fp8 latent dims = dv
@@ -72,15 +73,12 @@ __device__ inline void fp8x4_to_f32(int v, float f[4]) {
   f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
 }
 
-// 4 packed e4m3fn bytes -> 4 bf16 in two dwords (exact: every e4m3fn value is a
-// bf16 value, so the high half of the f32 is the bf16).
+// 4 packed e4m3fn bytes -> 4 bf16 in two dwords with the gfx950 converter
+// (scale 1.0; exact, since every e4m3fn value is a bf16 value).
 __device__ inline i32x2 fp8x4_to_bf16x4(int v) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-  i32x2 r;
-  r.x = __builtin_amdgcn_perm(__builtin_bit_cast(int, lo.y), __builtin_bit_cast(int, lo.x), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__builtin_bit_cast(int, hi.y), __builtin_bit_cast(int, hi.x), 0x07060302u);
-  return r;
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true);
+  return i32x2{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
 }
 
 // 4 floats -> 4 packed e4m3fn bytes (round to nearest even).
@@ -302,14 +300,16 @@ __device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u) 
     }
     return i32x2{(int)w[0], (int)w[1]};
   } else {
-    // ds_read_b64_tr_b8: within each group of 8 lanes, lane e supplies the
-    // address of an 8-byte row segment and every lane i of the group receives
-    // byte i of each segment, in lane order. Group G = lane/8 covers dv
-    // 32*blk + 8*(G%4) + (lane%8); lane e of it supplies key 16u + tr_key(e, h).
-    const int G = lane >> 3, e = lane & 7;
-    const int key = 16 * u + tr_key(e, h);
-    const int dv0 = 32 * blk + 8 * (G & 3);
-    const int off = key * kNope + (swz(key, dv0 >> 4) << 4) + (dv0 & 15);
+    // ds_read_b64_tr_b8 transposes within groups of 16 lanes: lane s of a group
+    // supplies the address of an 8-byte row segment, and lane i of the group
+    // receives, as its byte j, byte (i % 8) of the segment supplied by lane
+    // 2j + i/8. Group g = lane/16 covers dv 32*blk + 16*(g%2) + (lane%16), so
+    // its lanes 2j and 2j+1 supply key 16u + tr_key(j, h) at dv offsets 0 and 8
+    // of that 16-wide slice (one 16-byte LDS chunk).
+    const int g = lane >> 4, sup = lane & 15;
+    const int key = 16 * u + tr_key(sup >> 1, h);
+    const int chunk = 2 * blk + (g & 1);
+    const int off = key * kNope + (swz(key, chunk) << 4) + 8 * (sup & 1);
     typedef int v2i_lds __attribute__((ext_vector_type(2)));
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
         (__attribute__((address_space(3))) v2i_lds*)(nope + off));

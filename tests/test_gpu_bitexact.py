@@ -37,7 +37,7 @@ def test_decode_odd_length_tail():
 @pytest.mark.parametrize("shape", [(1, 1, 16, 576), (2, 2, 64, 576), (3, 2, 16, 512)])
 def test_query_quantization_matches_oracle(shape):
     w = workloads.make("tiny", batch=shape[0], s_q=shape[1], h_q=shape[2],
-                       d_rope=(shape[3] - 512) // 2, seq_len=64, seed=sum(shape))
+                       d_rope=shape[3] - 512, seq_len=64, seed=sum(shape))
     qb = w.q_bits.copy()
     flat = qb.reshape(-1, shape[3])
     flat[0, :512] = 0                                           # an all-zero row
