@@ -121,26 +121,54 @@ __device__ inline int q_exponent(float amax) {
 
 constexpr int kNopeRegion = kKeys * kNope;          // 32 KiB per buffer
 constexpr int kRopeRegion = kKeys * 128;            // 8 KiB per buffer
-constexpr int kRopeBase = 2 * kNopeRegion;          // rope regions after both nope regions
+constexpr int kBufs = 3;                            // LDS ring: 1 tile computing, 2 landing
+constexpr int kRopeBase = kBufs * kNopeRegion;      // rope regions after all nope regions
 
 template <int ROPE>
 struct Tile {
-  static constexpr int lds_bytes = 2 * kNopeRegion + (ROPE > 0 ? 2 * kRopeRegion : 0);
+  static constexpr int lds_bytes = kBufs * kNopeRegion + (ROPE > 0 ? kBufs * kRopeRegion : 0);
+  // global->LDS loads one wave issues for a full tile
+  template <int NW> static constexpr int loads_per_wave() { return (32 + (ROPE > 0 ? 8 : 0)) / NW; }
 };
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 __device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
 // One 16-byte-per-lane global->LDS direct load: lane l's 16 bytes from `src`
-// land at lds_base + 16 l (lds_base must be wave-uniform).
+// land at lds_base + 16 l (lds_base must be wave-uniform; it goes to M0).
+// Written as inline asm so the compiler does not treat every later LDS read
+// as possibly aliasing the in-flight copy (it would then wait for all
+// outstanding loads, draining the prefetch ring); the tile loop orders the
+// copies with explicit vmcnt waits and a barrier instead.
 __device__ inline void load_lds16(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+  const unsigned m0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
 }
+
+// Max of a value over lanes l and l ^ 32 (the two halves holding one query row).
+__device__ inline float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
 // Wave index within the workgroup, as a wave-uniform (scalar) value.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 __device__ inline i32x4 lds_ld16(const uint8_t* base, int off) {
   return *reinterpret_cast<const i32x4*>(base + off);
+}
+
+// ds_read_b64_tr_b8 at base + off (see vt_bytes for the lane semantics).
+__device__ inline i32x2 lds_tr8(const uint8_t* base, int off) {
+  typedef int v2i_lds __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_lds*)(base + off));
 }
 
 // Per-lane byte offsets (within a 64-row page) of the 16-byte chunks a lane
@@ -171,14 +199,19 @@ struct LoadOffsets {
 // compiler cannot see through: otherwise it hoists the 40 per-load addresses
 // (or the offsets) out of the tile loop and spills them.
 template <int ROPE>
-__device__ inline LoadOffsets<ROPE> fresh_offsets(int lane) {
+__device__ inline LoadOffsets<ROPE> fresh_offsets(int) {
+  // lane id from the exec-mask bit count: no register kept alive for it
+  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   asm volatile("" : "+v"(lane));
   return LoadOffsets<ROPE>(lane);
 }
 
 // Issue the global->LDS copies of one 64-key tile into buffer `bufi`.
 // Dense tiles read one page: `page_base` points at its first row and rows
-// >= `valid` are zero-filled instead of loaded (the page's slack).
+// >= `valid` are zero-filled instead of loaded (the page's slack). A full
+// tile issues exactly Tile::loads_per_wave loads per wave, which the tile
+// loop's vmcnt waits count on; a partial tile issues a data-dependent number
+// and therefore drains all outstanding loads before returning.
 template <int ROPE, int NW>
 __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* page_base, int valid,
                                         int lane, int wave) {
@@ -216,6 +249,7 @@ __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* p
           *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
       }
     }
+    wait_vmcnt<0>();
   }
 }
 
@@ -286,7 +320,7 @@ __device__ inline int tr_key(int e, int h) {
 // V^T bytes for dv block blk (32 dv values) and contraction bytes 8u .. 8u+7:
 // byte e of the result is V[16u + tr_key(e, h)][32*blk + n] (e4m3fn).
 template <bool GATHER>
-__device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u) {
+__device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u, const int* vt_base) {
   const int h = lane >> 5;
   if constexpr (GATHER) {
     const int n = lane & 31;
@@ -306,15 +340,41 @@ __device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u) 
     // 2j + i/8. Group g = lane/16 covers dv 32*blk + 16*(g%2) + (lane%16), so
     // its lanes 2j and 2j+1 supply key 16u + tr_key(j, h) at dv offsets 0 and 8
     // of that 16-wide slice (one 16-byte LDS chunk).
-    const int g = lane >> 4, sup = lane & 15;
-    const int key = 16 * u + tr_key(sup >> 1, h);
-    const int chunk = 2 * blk + (g & 1);
-    const int off = key * kNope + (swz(key, chunk) << 4) + 8 * (sup & 1);
-    typedef int v2i_lds __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) v2i_lds*)(nope + off));
+    // lanes 2j, 2j+1 of group g supply key 16u + tr_key(j, h) at dv chunk
+    // 2*blk + g%2, bytes 0-7 / 8-15 (see LdsBases::vt)
+    return lds_tr8(nope, vt_base[blk & 3] + 8192 * u + 128 * (blk >> 2));
   }
 }
+
+// Per-lane LDS byte offsets of every fragment read, split as (one of four
+// lane bases) + (compile-time offset). The chunk swizzle only permutes the low
+// three chunk bits, so the loop-varying part of each chunk index (bits 3-4)
+// becomes an immediate offset and only the low bits enter the bases:
+//  * fp8 K fragment t, half e:  (32 kb + krow)*512 + 16*((4t + 2h + e) ^ (krow & 7))
+//      = k8[t & 1][e] + 32*kb*512 + 128*(t >> 1)
+//  * bf16 K fragment t (16 B): = k16[t & 3] + 32*kb*512 + 128*(t >> 2)
+//  * rope fragment t:           = rp[t] + 32*kb*128           (rope region)
+//  * V^T read (blk, u):         = vt[blk & 3] + 8192*u + 128*(blk >> 2)
+struct LdsBases {
+  int k8[2][2], k16[4], rp[4], vt[4];
+  __device__ LdsBases(int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    const int krow = key_of_row(n), kx = krow & 7;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) k8[p][e] = krow * kNope + (((4 * p + 2 * h + e) ^ kx) << 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      k16[t] = krow * kNope + (((2 * t + h) ^ kx) << 4);
+      rp[t] = krow * 128 + (((2 * t + h) ^ kx) << 4);
+    }
+    const int g = lane >> 4, sup = lane & 15;
+    const int tk = tr_key(sup >> 1, h);
+#pragma unroll
+    for (int b3 = 0; b3 < 4; ++b3) vt[b3] = tk * kNope + (((2 * b3 + (g & 1)) ^ (tk & 7)) << 4) + 8 * (sup & 1);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // The S^T = K Q^T products accumulate in VGPRs (inline asm with "v" operands),
@@ -389,19 +449,17 @@ struct KDims {
 // halves (lanes n and n+32). Fragment t (K = 64 dims 64t .. 64t+63) holds dims
 // 64t + 32h + (0..31) in byte order.
 __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 qn[8], int& e_out) {
-  unsigned raw[8][16];
+  // Two passes over the row (the second hits the cache) instead of holding
+  // its 256 bf16 values in 128 registers next to the 64-register result.
   float amax = 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+      const i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const unsigned w = (unsigned)v[d];
-        raw[t][4 * k + d] = w;
-        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
-      }
+      for (int d = 0; d < 4; ++d)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo((unsigned)v[d])), fabsf(bf16_hi((unsigned)v[d]))));
     }
   }
   amax = fmaxf(amax, __shfl_xor(amax, 32));
@@ -410,10 +468,11 @@ __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 q
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const unsigned w0 = raw[t][2 * d], w1 = raw[t][2 * d + 1];
-      qn[t][d] = f32x4_to_fp8x4(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
-                                bf16_hi(w1) * inv);
+    for (int k = 0; k < 4; ++k) {
+      const i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+      const unsigned w0 = (unsigned)v[0], w1 = (unsigned)v[1], w2 = (unsigned)v[2], w3 = (unsigned)v[3];
+      qn[t][2 * k] = f32x4_to_fp8x4(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv, bf16_hi(w1) * inv);
+      qn[t][2 * k + 1] = f32x4_to_fp8x4(bf16_lo(w2) * inv, bf16_hi(w2) * inv, bf16_lo(w3) * inv, bf16_hi(w3) * inv);
     }
   }
   e_out = e;
@@ -494,16 +553,20 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     issue_dense_tile<ROPE, NW>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, lane, wave);
   };
 
-  int page_cur = -1, page_next = -1;   // dense
-  int row_cur = -1, row_next = -1;     // sparse: this lane's tile row
+  // Dense tiles are loaded two ahead (tiles k+1 and k+2 land while tile k
+  // computes); sparse tiles one ahead.
+  int page_cur = -1, page_next = -1, page_next2 = -1;   // dense
+  int row_cur = -1, row_next = -1;                      // sparse: this lane's tile row
   if (ntiles > 0) {
     if constexpr (SPARSE) {
       row_cur = sparse_row(u0 * kKeys + lane);
       issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
     } else {
       page_cur = page_of(u0);
-      issue_dense(u0, page_cur, 0);
       page_next = page_of(u0 + 1);
+      issue_dense(u0, page_cur, 0);
+      if (ntiles > 1) issue_dense(u0 + 1, page_next, 1);
+      page_next2 = page_of(u0 + 2);
     }
   }
 
@@ -537,9 +600,13 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
   }
 
-  // The K operand's row m = n is tile key krow (+ 32 kb); krow & 7 is fixed
-  // per lane, so chunk positions are the logical chunks XOR krow & 7.
-  const int krow = key_of_row(n);
+  // All query loads are complete before the tile loop: the tile copies are
+  // inline asm the compiler does not count, and without this it would wait
+  // for every outstanding copy before the first use of a query register in
+  // each tile.
+  wait_vmcnt<0>();
+
+  const LdsBases lb(lane);
 
   f32x16 O[16];
 #pragma unroll
@@ -547,22 +614,33 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   float m_run = -INFINITY;   // max used for the exponentials (log2 domain)
   float l_run = 0.f;         // this lane's share of the running sum
 
+  int buf = 0;   // k % kBufs
   for (int k = 0; k < ntiles; ++k) {
-    wait_tile_and_sync();
+    // Tile k has landed once at most one later tile's loads are outstanding;
+    // the barrier then also frees the buffer of tile k-1 for tile k+2.
+    if constexpr (SPARSE) {
+      wait_vmcnt<0>();
+    } else {
+      if (k + 1 < ntiles) wait_vmcnt<Tile<ROPE>::template loads_per_wave<NW>()>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const int buf_next = buf == kBufs - 1 ? 0 : buf + 1;
+    const int buf_next2 = buf_next == kBufs - 1 ? 0 : buf_next + 1;
     if constexpr (SPARSE) {
       if (k + 1 < ntiles) {
         row_next = sparse_row((u0 + k + 1) * kKeys + lane);
-        issue_sparse_tile<ROPE, NW>(lds, (k + 1) & 1, kv, row_next, lane, wave);
+        issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
       }
     } else {
-      if (k + 1 < ntiles) issue_dense(u0 + k + 1, page_next, (k + 1) & 1);
+      if (k + 2 < ntiles) issue_dense(u0 + k + 2, page_next2, buf_next2);
     }
     // A wave whose row block lies past the last row (ragged row counts) runs
     // the same code on zero queries and only skips the stores: a second loop
     // path around the accumulators makes the register allocator shuffle them.
-    const int page_after = SPARSE ? -1 : page_of(u0 + k + 2);
-    const uint8_t* nope = lds + (k & 1) * kNopeRegion;
-    const uint8_t* rope = lds + kRopeBase + (k & 1) * kRopeRegion;
+    const int page_after = SPARSE ? -1 : page_of(u0 + k + 3);
+    const uint8_t* nope = lds + buf * kNopeRegion;
+    const uint8_t* rope = lds + kRopeBase + buf * kRopeRegion;
     const int unit = u0 + k;
 
     // ---- S^T = K Q^T -------------------------------------------------------
@@ -573,11 +651,11 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 acc = f32x16{};
-      const int row_off = (32 * kb + krow) * kNope;
       if constexpr (DOT == DOT_FP8) {
         auto kfrag = [&](int t) -> i32x8 {
-          const i32x4 lo = lds_ld16(nope, row_off + (swz(krow, 4 * t + 2 * h) << 4));
-          const i32x4 hi = lds_ld16(nope, row_off + (swz(krow, 4 * t + 2 * h + 1) << 4));
+          const int c = 32 * kb * kNope + 128 * (t >> 1);
+          const i32x4 lo = lds_ld16(nope, lb.k8[t & 1][0] + c);
+          const i32x4 hi = lds_ld16(nope, lb.k8[t & 1][1] + c);
           return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         };
         i32x8 nxt = kfrag(0);
@@ -590,11 +668,12 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        i32x4 nxt = lds_ld16(nope, row_off + (swz(krow, h) << 4));
+        auto kfrag16 = [&](int t) -> i32x4 { return lds_ld16(nope, lb.k16[t & 3] + 32 * kb * kNope + 128 * (t >> 2)); };
+        i32x4 nxt = kfrag16(0);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           const i32x4 raw = nxt;
-          if (t + 1 < 16) nxt = lds_ld16(nope, row_off + (swz(krow, 2 * (t + 1) + h) << 4));
+          if (t + 1 < 16) nxt = kfrag16(t + 1);
           const i32x2 b0 = fp8x4_to_bf16x4(raw.x), b1 = fp8x4_to_bf16x4(raw.y);
           const i32x2 b2 = fp8x4_to_bf16x4(raw.z), b3 = fp8x4_to_bf16x4(raw.w);
           const bf16x8 a0 = __builtin_bit_cast(bf16x8, i32x4{b0.x, b0.y, b1.x, b1.y});
@@ -609,7 +688,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       if constexpr (ROPE > 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const i32x4 raw = lds_ld16(rope, (32 * kb + krow) * 128 + (swz(krow, 2 * t + h) << 4));
+          const i32x4 raw = lds_ld16(rope, lb.rp[t] + 32 * kb * 128);
           if (t == 0) mfma_bf16_32x32x16_after_valu(acc, __builtin_bit_cast(bf16x8, raw), qr[t]);
           else mfma_bf16_32x32x16(acc, __builtin_bit_cast(bf16x8, raw), qr[t]);
         }
@@ -619,10 +698,19 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
 
     // ---- mask + online softmax (log2 domain) --------------------------------
+    // Tile-wide visibility: a tile every row of the workgroup sees in full
+    // skips the per-element mask (all but the last tile of a sequence).
+    bool full;
+    int limit = 0;    // dense: keys of this tile this lane's row may see
     unsigned long long smask = 0;
-    bool page_ok = true;
-    if constexpr (SPARSE) smask = __ballot(row_cur >= 0);
-    else page_ok = page_valid(page_cur);
+    if constexpr (SPARSE) {
+      smask = __ballot(row_cur >= 0);
+      full = smask == ~0ull;
+    } else {
+      const bool page_ok = page_valid(page_cur);
+      full = page_ok && (unit + 1) * kKeys <= sk - (a.causal ? a.s_q - 1 : 0);
+      limit = page_ok ? row_len - unit * kKeys : 0;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -632,13 +720,14 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         const int key = 32 * kb + 8 * j + 4 * ((j + h) & 1) + (r & 3);
         bool valid;
         if constexpr (SPARSE) valid = (smask >> key) & 1ull;
-        else valid = page_ok && (unit * kKeys + key < row_len);
-        const float z = valid ? S[kb][r] * a.sm_log2 : -INFINITY;
+        else valid = key < limit;
+        const float zs = S[kb][r] * a.sm_log2;
+        const float z = (full || valid) ? zs : -INFINITY;
         S[kb][r] = z;
         mx = fmaxf(mx, z);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const bool raise = mx > m_run + Soft<DOT>::tau;
     if (__ballot(raise)) {
       const float m_new = raise ? mx : m_run;
@@ -679,7 +768,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         i32x8 av;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const i32x2 v = vt_bytes<GATHER_V>(nope, lane, blk, u);
+          const i32x2 v = vt_bytes<GATHER_V>(nope, lane, blk, u, lb.vt);
           av[2 * u] = v.x;
           av[2 * u + 1] = v.y;
         }
@@ -708,7 +797,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       for (int blk = 0; blk < 16; ++blk) {
         i32x2 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = vt_bytes<GATHER_V>(nope, lane, blk, u);
+        for (int u = 0; u < 4; ++u) v[u] = vt_bytes<GATHER_V>(nope, lane, blk, u, lb.vt);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const i32x2 lo = fp8x4_to_bf16x4(v[u].x), hi = fp8x4_to_bf16x4(v[u].y);
@@ -719,8 +808,10 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       }
     }
     page_cur = page_next;
-    page_next = page_after;
+    page_next = page_next2;
+    page_next2 = page_after;
     row_cur = row_next;
+    buf = buf_next;
   }
 
   if (!wave_active) return;
