@@ -157,11 +157,13 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   d.splits = splits;
   d.softmax_scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.f / sqrtf((float)(p->d_nope + p->d_rope));
   const size_t frags = (size_t)splits * d.groups * d.row_blocks;
-  d.part_o = need > 0 ? static_cast<float*>(ws) : nullptr;
-  d.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + frags * 16 * 64 * 16 * sizeof(float))
+  d.part_o = need > 0 ? static_cast<uint16_t*>(ws) : nullptr;
+  d.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + frags * 16 * 64 * 16 * sizeof(uint16_t))
                         : nullptr;
   const char* gv = getenv("MLA_FP8_GATHER_V");
   d.gather_v = gv != nullptr && gv[0] == '1';
+  const char* rk = getenv("MLA_FP8_ROWS_KERNEL");
+  d.rows_kernel = rk != nullptr && rk[0] == '1';
   const char* dbg = getenv("MLA_FP8_DEBUG");
   d.debug_print = dbg != nullptr && dbg[0] == '1';
   if (d.debug_print)

@@ -19,7 +19,7 @@ struct DecodeLaunch {
   const float* v_scale;
   uint16_t* out;
   float* lse;
-  float* part_o;    // workspace, splits > 1
+  uint16_t* part_o; // workspace, splits > 1: fp16 partial outputs
   float* part_lse;  // workspace, splits > 1
   int32_t batch, s_q, h_q, d_rope;
   int32_t num_pages, max_pages, topk, causal, dot;
@@ -29,6 +29,7 @@ struct DecodeLaunch {
   int32_t splits;
   float softmax_scale;
   bool gather_v;       // debug: byte-gather V^T fragments instead of transposed LDS reads
+  bool rows_kernel;    // fp8 dots: P.V split by row block (as for bf16 dots) instead of by dv
   bool debug_print;
 };
 

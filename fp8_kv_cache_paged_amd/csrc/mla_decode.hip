@@ -87,6 +87,14 @@ __device__ inline int f32x4_to_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
 }
 
+// Two floats as two IEEE half values (round to nearest even), a in the low half.
+__device__ inline unsigned half2_bits(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (unsigned)__builtin_bit_cast(uint16_t, ha) | ((unsigned)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ inline float half_lo(unsigned w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float half_hi(unsigned w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 __device__ inline unsigned bf16x2_bits(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
   return (unsigned)__builtin_bit_cast(unsigned short, x) |
@@ -112,11 +120,14 @@ __device__ inline int q_exponent(float amax) {
 // (0 and 32 KiB), then the rope regions (64 and 72 KiB), which keeps every
 // nope fragment offset inside the 16-bit ds_read immediate.
 //
-// Within a row, 16-byte chunk c is stored at chunk position c ^ (row & 7).
-// Rows are 0 mod 32 banks apart, so without the swizzle the same column of 8
-// rows would hit the same banks; with it, 8 consecutive rows (or any 8 rows
-// with distinct row & 7) spread over all 32 banks. Only the low three bits of
-// the chunk index are permuted, so each fragment read below needs at most four
+// Within a nope row, 16-byte chunk c is stored at chunk position c ^ (row & 15);
+// within a rope row at c ^ ((row >> 1) & 7). The LDS has 64 banks of 4 bytes and
+// serves a 16-byte-per-lane read 16 lanes at a time; nope rows are a multiple
+// of 256 bytes apart, so without the swizzle one column of 16 rows would hit
+// the same 4 banks, and with it any 16 rows with distinct row & 15 cover all 64
+// banks. Rope rows are 128 bytes, two per 256-byte bank line: row & 1 already
+// separates the two, and (row >> 1) & 7 the eight lines. Only the low four
+// chunk bits are permuted, so each fragment read below needs at most eight
 // per-lane base addresses plus compile-time offsets.
 
 constexpr int kNopeRegion = kKeys * kNope;          // 32 KiB per buffer
@@ -139,7 +150,8 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ inline int swz(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ inline int swz(int row, int chunk) { return chunk ^ (row & 15); }
+__device__ inline int swz_rope(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // One 16-byte-per-lane global->LDS direct load: lane l's 16 bytes from `src`
 // land at lds_base + 16 l (lds_base must be wave-uniform; it goes to M0).
@@ -172,27 +184,28 @@ __device__ inline i32x2 lds_tr8(const uint8_t* base, int off) {
 }
 
 // Per-lane byte offsets (within a 64-row page) of the 16-byte chunks a lane
-// moves. Nope load j covers rows 2j, 2j+1 (lane l: row 2j + l/32, chunk
-// position l%32); (2j + l/32) & 7 only depends on j & 3, so four offsets serve
-// all 32 loads: off(j) = nope_lane(j & 3) + 2j * RB. Rope load j covers rows
-// 8j .. 8j+7 (row 8j + l/8, position l%8): off(j) = rope_lane + 8j * RB.
-// Wave w issues the contiguous block of loads w*(32/NW) .., so j & 3 is known
-// at compile time.
+// moves: the lane at chunk position P of row r fetches the row's chunk
+// P ^ swizzle(r). Nope load j covers rows 2j, 2j+1 (lane l: row 2j + l/32,
+// position l%32); (2j + l/32) & 15 only depends on j & 7, so eight offsets
+// serve all 32 loads: off(j) = nope_lane(j & 7) + 2j * RB. Rope load j covers
+// rows 8j .. 8j+7 (row 8j + l/8, position l%8), whose ((row >> 1) & 7) only
+// depends on j & 1: off(j) = rope_lane[j & 1] + 8j * RB. Wave w issues the
+// contiguous block of loads w*(32/NW) .. (a multiple of 8 nope and of 2 rope
+// loads), so j & 7 and j & 1 are known at compile time.
 template <int ROPE>
 struct LoadOffsets {
-  int n0, n1, n2, n3;
-  int rope_lane;
+  int nv[8];          // nope load j: global chunk offset for rows with (2j + hi) & 15
+  int rope_lane[2];   // rope load j: by j & 1
   __device__ LoadOffsets(int lane) {
     constexpr int RB = kNope + 2 * ROPE;
     const int hi = lane >> 5, p = lane & 31;
-    n0 = hi * RB + ((p ^ (0 + hi)) << 4);
-    n1 = hi * RB + ((p ^ (2 + hi)) << 4);
-    n2 = hi * RB + ((p ^ (4 + hi)) << 4);
-    n3 = hi * RB + ((p ^ (6 + hi)) << 4);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) nv[v] = hi * RB + ((p ^ (2 * v + hi)) << 4);
     const int r8 = lane >> 3, p8 = lane & 7;
-    rope_lane = r8 * RB + kNope + ((p8 ^ r8) << 4);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) rope_lane[par] = r8 * RB + kNope + ((p8 ^ (4 * par + (r8 >> 1))) << 4);
   }
-  __device__ int nope_lane(int v) const { return v == 0 ? n0 : v == 1 ? n1 : v == 2 ? n2 : n3; }
+  __device__ int nope_lane(int v) const { return nv[v]; }
 };
 
 // The offsets are recomputed for every tile from a copy of the lane id the
@@ -200,9 +213,10 @@ struct LoadOffsets {
 // (or the offsets) out of the tile loop and spills them.
 template <int ROPE>
 __device__ inline LoadOffsets<ROPE> fresh_offsets(int) {
-  // lane id from the exec-mask bit count: no register kept alive for it
-  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  asm volatile("" : "+v"(lane));
+  // lane id from the exec-mask bit count, as volatile asm so that it is
+  // recomputed here rather than hoisted out of the loop (and spilled)
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   return LoadOffsets<ROPE>(lane);
 }
 
@@ -226,17 +240,17 @@ __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* p
   if (valid == kKeys) {
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
-      load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 3)), nope + jj * 1024);
+      load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 7)), nope + jj * 1024);
     if constexpr (ROPE > 0) {
 #pragma unroll
       for (int jj = 0; jj < RJ; ++jj)
-        load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane), rope + jj * 1024);
+        load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane[jj & 1]), rope + jj * 1024);
     }
   } else {
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       if (row0 + 2 * jj < valid)
-        load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 3)), nope + jj * 1024);
+        load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 7)), nope + jj * 1024);
       else
         *reinterpret_cast<i32x4*>(nope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
     }
@@ -244,7 +258,7 @@ __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* p
 #pragma unroll
       for (int jj = 0; jj < RJ; ++jj) {
         if (rrow0 + 8 * jj < valid)
-          load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane), rope + jj * 1024);
+          load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane[jj & 1]), rope + jj * 1024);
         else
           *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
       }
@@ -269,7 +283,7 @@ __device__ inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* 
   for (int jj = 0; jj < NJ; ++jj) {
     const int cr = __shfl(mine, row0 + 2 * jj);
     if (cr >= 0)
-      load_lds16(kv + (long)cr * RB + (lo.nope_lane(jj & 3) - (lane >> 5) * RB), nope + jj * 1024);
+      load_lds16(kv + (long)cr * RB + (lo.nope_lane(jj & 7) - (lane >> 5) * RB), nope + jj * 1024);
     else
       *reinterpret_cast<i32x4*>(nope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
   }
@@ -278,10 +292,34 @@ __device__ inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* 
     for (int jj = 0; jj < RJ; ++jj) {
       const int cr = __shfl(mine, rrow0 + 8 * jj);
       if (cr >= 0)
-        load_lds16(kv + (long)cr * RB + (lo.rope_lane - (lane >> 3) * RB), rope + jj * 1024);
+        load_lds16(kv + (long)cr * RB + (lo.rope_lane[jj & 1] - (lane >> 3) * RB), rope + jj * 1024);
       else
         *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
     }
+  }
+}
+
+// One of the Tile::loads_per_wave copies that issue_dense_tile makes for a
+// full dense tile (load jj of this wave; jj is a compile-time constant at the
+// call sites), so that the copies can be spread between other instructions.
+// The lane offset is recomputed each time (volatile asm: not hoisted and kept).
+template <int ROPE, int NW>
+__device__ inline void issue_dense_load(uint8_t* lds, int bufi, const uint8_t* page_base, int jj, int wave) {
+  constexpr int RB = kNope + 2 * ROPE;
+  constexpr int NJ = 32 / NW, RJ = 8 / NW;
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  if (jj < NJ) {
+    const int hi = lane >> 5, p = lane & 31;
+    const int off = hi * RB + ((p ^ (2 * (jj & 7) + hi)) << 4);
+    load_lds16(page_base + (unsigned)(wave * NJ * 2 * RB + 2 * jj * RB + off),
+               lds + bufi * kNopeRegion + (wave * NJ + jj) * 1024);
+  } else {
+    const int r = jj - NJ;
+    const int r8 = lane >> 3, p8 = lane & 7;
+    const int off = r8 * RB + kNope + ((p8 ^ (4 * (r & 1) + (r8 >> 1))) << 4);
+    load_lds16(page_base + (unsigned)(wave * RJ * 8 * RB + 8 * r * RB + off),
+               lds + kRopeBase + bufi * kRopeRegion + (wave * RJ + r) * 1024);
   }
 }
 
@@ -320,7 +358,7 @@ __device__ inline int tr_key(int e, int h) {
 // V^T bytes for dv block blk (32 dv values) and contraction bytes 8u .. 8u+7:
 // byte e of the result is V[16u + tr_key(e, h)][32*blk + n] (e4m3fn).
 template <bool GATHER>
-__device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u, const int* vt_base) {
+__device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u, int vt_base) {
   const int h = lane >> 5;
   if constexpr (GATHER) {
     const int n = lane & 31;
@@ -339,40 +377,41 @@ __device__ inline i32x2 vt_bytes(const uint8_t* nope, int lane, int blk, int u, 
     // receives, as its byte j, byte (i % 8) of the segment supplied by lane
     // 2j + i/8. Group g = lane/16 covers dv 32*blk + 16*(g%2) + (lane%16), so
     // its lanes 2j and 2j+1 supply key 16u + tr_key(j, h) at dv offsets 0 and 8
-    // of that 16-wide slice (one 16-byte LDS chunk).
-    // lanes 2j, 2j+1 of group g supply key 16u + tr_key(j, h) at dv chunk
-    // 2*blk + g%2, bytes 0-7 / 8-15 (see LdsBases::vt)
-    return lds_tr8(nope, vt_base[blk & 3] + 8192 * u + 128 * (blk >> 2));
+    // of that 16-wide slice (one 16-byte LDS chunk); vt_base is
+    // vt_lane_base(lane, blk % 8).
+    return lds_tr8(nope, vt_base + 8192 * u + 256 * (blk >> 3));
   }
 }
 
-// Per-lane LDS byte offsets of every fragment read, split as (one of four
+// Per-lane LDS byte offsets of every fragment read, split as (one of eight
 // lane bases) + (compile-time offset). The chunk swizzle only permutes the low
-// three chunk bits, so the loop-varying part of each chunk index (bits 3-4)
+// four chunk bits, so the loop-varying part of each chunk index (bit 4)
 // becomes an immediate offset and only the low bits enter the bases:
-//  * fp8 K fragment t, half e:  (32 kb + krow)*512 + 16*((4t + 2h + e) ^ (krow & 7))
-//      = k8[t & 1][e] + 32*kb*512 + 128*(t >> 1)
-//  * bf16 K fragment t (16 B): = k16[t & 3] + 32*kb*512 + 128*(t >> 2)
+//  * fp8 K fragment t, half e:  (32 kb + krow)*512 + 16*((4t + 2h + e) ^ (krow & 15))
+//      = k8[t & 3][e] + 32*kb*512 + 256*(t >> 2)
+//  * bf16 K fragment t (16 B): = k16[t & 7] + 32*kb*512 + 256*(t >> 3)
 //  * rope fragment t:           = rp[t] + 32*kb*128           (rope region)
-//  * V^T read (blk, u):         = vt[blk & 3] + 8192*u + 128*(blk >> 2)
+//  * V^T read (blk, u):         = vt_base(blk & 7) + 8192*u + 256*(blk >> 3)
+__device__ inline int vt_lane_base(int lane, int b8) {
+  const int h = lane >> 5, g = lane >> 4, sup = lane & 15;
+  const int tk = tr_key(sup >> 1, h);
+  return tk * kNope + (((2 * b8 + (g & 1)) ^ (tk & 15)) << 4) + 8 * (sup & 1);
+}
 struct LdsBases {
-  int k8[2][2], k16[4], rp[4], vt[4];
+  int k8[4][2], k16[8], rp[4], vt[8];
   __device__ LdsBases(int lane) {
     const int n = lane & 31, h = lane >> 5;
-    const int krow = key_of_row(n), kx = krow & 7;
+    const int krow = key_of_row(n), kx = krow & 15, rx = (krow >> 1) & 7;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
       for (int e = 0; e < 2; ++e) k8[p][e] = krow * kNope + (((4 * p + 2 * h + e) ^ kx) << 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      k16[t] = krow * kNope + (((2 * t + h) ^ kx) << 4);
-      rp[t] = krow * 128 + (((2 * t + h) ^ kx) << 4);
-    }
-    const int g = lane >> 4, sup = lane & 15;
-    const int tk = tr_key(sup >> 1, h);
+    for (int t = 0; t < 8; ++t) k16[t] = krow * kNope + (((2 * t + h) ^ kx) << 4);
 #pragma unroll
-    for (int b3 = 0; b3 < 4; ++b3) vt[b3] = tk * kNope + (((2 * b3 + (g & 1)) ^ (tk & 7)) << 4) + 8 * (sup & 1);
+    for (int t = 0; t < 4; ++t) rp[t] = krow * 128 + (((2 * t + h) ^ rx) << 4);
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) vt[b8] = vt_lane_base(lane, b8);
   }
 };
 
@@ -398,9 +437,44 @@ __device__ inline void mfma_bf16_32x32x16(f32x16& acc, const bf16x8& a, const bf
 __device__ inline void mfma_bf16_32x32x16_after_valu(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// First product of an accumulator chain: C = 0 as an inline constant, so no
+// VALU zeroing (and no wait states after it) is needed.
+__device__ inline void mfma_fp8_32x32x64_first(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_32x32x16_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_32x32x16_first_after_valu(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+// Two chained bf16 products whose A operands were both just converted by
+// VALU. One statement, so that no conversion can be scheduled between them
+// (an MFMA reading a register VALU wrote without wait states reads stale data).
+__device__ inline void mfma_bf16_pair_after_valu(f32x16& acc, const bf16x8& a0, const bf16x8& b0,
+                                                 const bf16x8& a1, const bf16x8& b1) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+               : "+v"(acc) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+}
+__device__ inline void mfma_bf16_pair_first_after_valu(f32x16& acc, const bf16x8& a0, const bf16x8& b0,
+                                                       const bf16x8& a1, const bf16x8& b1) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %4, %0"
+               : "=&v"(acc) : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+}
+// Wait states before VALU reads of the four S^T accumulators (named as
+// operands so that no read of any of them can be scheduled above the wait).
+__device__ inline void s_nop_result4(f32x16& a0, f32x16& a1, f32x16& a2, f32x16& a3) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+}
+__device__ inline void s_nop_result2(f32x16& a0, f32x16& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+}
 // O^T += V^T P^T with the accumulator pinned to AGPRs ("a" operands).
 __device__ inline void mfma_fp8_32x32x64_acc(f32x16& acc, const i32x8& a, const i32x8& b) {
   asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_fp8_32x32x64_acc_after_valu(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_bf16_32x32x16_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
@@ -442,7 +516,7 @@ struct KDims {
       const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,      \
       const int32_t* __restrict__ indices, const float* __restrict__ k_scale,             \
       const float* __restrict__ v_scale, uint16_t* __restrict__ out, float* __restrict__ lse, \
-      float* __restrict__ part_o, float* __restrict__ part_lse
+      uint16_t* __restrict__ part_o, float* __restrict__ part_lse
 
 // Q staging for the fp8-dot path: lane (n, h) quantizes its half of query row
 // n's 512 nope dims. The row's power-of-two exponent needs the amax of both
@@ -481,17 +555,26 @@ __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 q
 // Softmax bookkeeping runs in the log2 domain with a lazily raised running
 // max: the max used for exponentials is only raised when a tile's max exceeds
 // it by more than tau, so the rescale of the 256 accumulator registers is rare.
-// Every p is then at most 2^tau; the fp8 path stores e4m3fn(p * pscale), with
-// 2^tau * pscale = 448 (the format's largest value), which keeps tail
-// probabilities down to about 2^-17 representable.
+// Every p is then at most 2^tau. The fp8 path stores e4m3fn(p * 2^ps_log2)
+// with 2^(tau + ps_log2) = 256 <= 448 (the format's largest value), the power
+// of two folded into the exponent (exp2(z - m + ps_log2)); the row sums are
+// kept in the same scaled units. Scaled probabilities stay normal down to
+// p = 2^-11 and representable down to 2^-14 below the running max; tau = 3
+// keeps the rescales of the accumulators rare.
 template <int DOT> struct Soft;
-template <> struct Soft<1> { static constexpr float tau = 1.f, pscale = 224.f; };
-template <> struct Soft<0> { static constexpr float tau = 8.f, pscale = 1.f; };
+#ifndef MLA_FP8_TAU
+#define MLA_FP8_TAU 3
+#endif
+template <> struct Soft<1> { static constexpr float tau = MLA_FP8_TAU, ps_log2 = 8 - MLA_FP8_TAU; };
+template <> struct Soft<0> { static constexpr float tau = 8.f, ps_log2 = 0.f; };
 
+// Decode with the P.V products split over the waves by row block: each wave
+// owns 32 query rows end to end (S^T, softmax, P.V over all 512 dv). Used for
+// bf16 dots, whose P^T operands are too large to exchange between waves.
 template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1)))
-void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
+void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   constexpr int D = kNope + ROPE;               // q row length
   __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes];
   uint8_t* const lds = lds_;
@@ -543,9 +626,13 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     return cr;
   };
-  // Dense: one page per tile; the page id of the tile after next is fetched
-  // one iteration early so its scalar load latency hides behind a tile.
+  // Dense: one page per tile. Inside the tile loop page ids come from a
+  // register holding 64 of them (lane i: tile 64c + i of the split), read with
+  // v_readlane: a scalar load there would share the counter of the LDS
+  // fragment reads and, completing out of order, force them to full waits.
   auto page_of = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  auto page_of_lane = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  int pages_v = -1;
   auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
   auto issue_dense = [&](int unit, int page, int bufi) {
     const bool ok = page_valid(page);
@@ -566,7 +653,6 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       page_next = page_of(u0 + 1);
       issue_dense(u0, page_cur, 0);
       if (ntiles > 1) issue_dense(u0 + 1, page_next, 1);
-      page_next2 = page_of(u0 + 2);
     }
   }
 
@@ -604,7 +690,9 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   // inline asm the compiler does not count, and without this it would wait
   // for every outstanding copy before the first use of a query register in
   // each tile.
+  if constexpr (!SPARSE) pages_v = page_of_lane(u0 + lane);
   wait_vmcnt<0>();
+  asm volatile("" : "+v"(pages_v));   // loaded before the loop, not inside it
 
   const LdsBases lb(lane);
 
@@ -633,69 +721,113 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
       }
     } else {
-      if (k + 2 < ntiles) issue_dense(u0 + k + 2, page_next2, buf_next2);
+      if (k + 2 < ntiles) {
+        const int t2 = k + 2;
+        if ((t2 & 63) == 0) {   // next 64 page ids (tile loops longer than 64 tiles)
+          pages_v = page_of_lane(u0 + t2 + lane);
+          wait_vmcnt<0>();
+        }
+        page_next2 = __builtin_amdgcn_readlane(pages_v, t2 & 63);
+        issue_dense(u0 + t2, page_next2, buf_next2);
+      }
     }
     // A wave whose row block lies past the last row (ragged row counts) runs
     // the same code on zero queries and only skips the stores: a second loop
     // path around the accumulators makes the register allocator shuffle them.
-    const int page_after = SPARSE ? -1 : page_of(u0 + k + 3);
     const uint8_t* nope = lds + buf * kNopeRegion;
     const uint8_t* rope = lds + kRopeBase + buf * kRopeRegion;
     const int unit = u0 + k;
 
     // ---- S^T = K Q^T -------------------------------------------------------
-    // Fragments are prefetched one MFMA ahead; the scheduling barriers keep
-    // the compiler from hoisting every fragment load of the tile (which would
-    // need up to 128 extra registers).
-    f32x16 S[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = f32x16{};
-      if constexpr (DOT == DOT_FP8) {
-        auto kfrag = [&](int t) -> i32x8 {
-          const int c = 32 * kb * kNope + 128 * (t >> 1);
-          const i32x4 lo = lds_ld16(nope, lb.k8[t & 1][0] + c);
-          const i32x4 hi = lds_ld16(nope, lb.k8[t & 1][1] + c);
-          return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        };
-        i32x8 nxt = kfrag(0);
-        asm volatile("s_nop 4" ::);   // acc was just zeroed by VALU
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const i32x8 cur = nxt;
-          if (t + 1 < 8) nxt = kfrag(t + 1);
-          mfma_fp8_32x32x64(acc, cur, qn[t]);
-          __builtin_amdgcn_sched_barrier(0);
+    // The fragment reads of a tile run through a ring several items deep, so
+    // about ten LDS reads are in flight while the MFMAs consume earlier ones
+    // (one wave per SIMD: nothing else hides the LDS latency). Items alternate
+    // between the two 32-key blocks, so consecutive MFMAs are independent. The
+    // rope products have accumulators of their own, since q_scale * k_scale
+    // applies to the nope products only; both are combined in the softmax.
+    // Scheduling barriers keep the compiler from hoisting the whole tile's
+    // fragment reads (which would need up to 160 more registers).
+    // (bf16 dots: the 128 registers of bf16 query fragments leave no room for
+    // separate rope accumulators; there the nope sums are scaled in place
+    // before the rope products are added to them.)
+    constexpr bool kSepRope = DOT == DOT_FP8 && ROPE > 0;
+    f32x16 Sn[2], Sr[2];
+    if constexpr (!kSepRope) Sr[0] = Sr[1] = f32x16{};
+    if constexpr (DOT == DOT_FP8) {
+      constexpr int NN = 16, NI = NN + (ROPE > 0 ? 8 : 0), PD = 5;
+      i32x4 rl[PD], rh[PD];
+      auto load = [&](int f) {
+        const int slot = f % PD, kb = f & 1;
+        if (f < NN) {
+          const int t = f >> 1;
+          const int c = 32 * kb * kNope + 256 * (t >> 2);
+          rl[slot] = lds_ld16(nope, lb.k8[t & 3][0] + c);
+          rh[slot] = lds_ld16(nope, lb.k8[t & 3][1] + c);
+        } else {
+          rl[slot] = lds_ld16(rope, lb.rp[(f - NN) >> 1] + 32 * kb * 128);
         }
-      } else {
-        auto kfrag16 = [&](int t) -> i32x4 { return lds_ld16(nope, lb.k16[t & 3] + 32 * kb * kNope + 128 * (t >> 2)); };
-        i32x4 nxt = kfrag16(0);
+      };
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const i32x4 raw = nxt;
-          if (t + 1 < 16) nxt = kfrag16(t + 1);
+      for (int f = 0; f < PD; ++f) load(f);
+#pragma unroll
+      for (int f = 0; f < NI; ++f) {
+        const int slot = f % PD, kb = f & 1;
+        const i32x4 lo = rl[slot], hi = rh[slot];
+        if (f + PD < NI) load(f + PD);
+        if (f < NN) {
+          const i32x8 kf = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          if (f < 2) mfma_fp8_32x32x64_first(Sn[kb], kf, qn[f >> 1]);
+          else mfma_fp8_32x32x64(Sn[kb], kf, qn[f >> 1]);
+        } else {
+          const bf16x8 kr = __builtin_bit_cast(bf16x8, lo);
+          if (f < NN + 2) mfma_bf16_32x32x16_first(Sr[kb], kr, qr[(f - NN) >> 1]);
+          else mfma_bf16_32x32x16(Sr[kb], kr, qr[(f - NN) >> 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // bf16 dots: each 16-byte fp8 read becomes two bf16 A operands.
+      constexpr int NN = 32, NI = NN + (ROPE > 0 ? 8 : 0), PD = 3;
+      i32x4 rl[PD];
+      auto load = [&](int f) {
+        const int kb = f & 1;
+        if (f < NN) {
+          const int t = f >> 1;
+          rl[f % PD] = lds_ld16(nope, lb.k16[t & 7] + 32 * kb * kNope + 256 * (t >> 3));
+        } else {
+          rl[f % PD] = lds_ld16(rope, lb.rp[(f - NN) >> 1] + 32 * kb * 128);
+        }
+      };
+#pragma unroll
+      for (int f = 0; f < PD; ++f) load(f);
+#pragma unroll
+      for (int f = 0; f < NI; ++f) {
+        const int kb = f & 1;
+        const i32x4 raw = rl[f % PD];
+        if (f + PD < NI) load(f + PD);
+        if (f < NN) {
+          const int t = f >> 1;
           const i32x2 b0 = fp8x4_to_bf16x4(raw.x), b1 = fp8x4_to_bf16x4(raw.y);
           const i32x2 b2 = fp8x4_to_bf16x4(raw.z), b3 = fp8x4_to_bf16x4(raw.w);
           const bf16x8 a0 = __builtin_bit_cast(bf16x8, i32x4{b0.x, b0.y, b1.x, b1.y});
           const bf16x8 a1 = __builtin_bit_cast(bf16x8, i32x4{b2.x, b2.y, b3.x, b3.y});
-          mfma_bf16_32x32x16_after_valu(acc, a0, qb[2 * t]);
-          mfma_bf16_32x32x16_after_valu(acc, a1, qb[2 * t + 1]);
-          __builtin_amdgcn_sched_barrier(0);
+          if (f < 2) mfma_bf16_pair_first_after_valu(Sn[kb], a0, qb[2 * t], a1, qb[2 * t + 1]);
+          else mfma_bf16_pair_after_valu(Sn[kb], a0, qb[2 * t], a1, qb[2 * t + 1]);
+        } else {
+          const bf16x8 kr = __builtin_bit_cast(bf16x8, raw);
+          if (f < NN + 2) mfma_bf16_32x32x16_after_valu(Sn[kb], kr, qr[(f - NN) >> 1]);
+          else mfma_bf16_32x32x16(Sn[kb], kr, qr[(f - NN) >> 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (ROPE > 0 && f == NN - 1) {
+          s_nop_result2(Sn[0], Sn[1]);
+          Sn[0] *= qk_scale;
+          Sn[1] *= qk_scale;
         }
       }
-      s_nop_result(acc);
-      acc *= qk_scale;
-      if constexpr (ROPE > 0) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const i32x4 raw = lds_ld16(rope, lb.rp[t] + 32 * kb * 128);
-          if (t == 0) mfma_bf16_32x32x16_after_valu(acc, __builtin_bit_cast(bf16x8, raw), qr[t]);
-          else mfma_bf16_32x32x16(acc, __builtin_bit_cast(bf16x8, raw), qr[t]);
-        }
-        s_nop_result(acc);
-      }
-      S[kb] = acc;
     }
+    if constexpr (kSepRope) s_nop_result4(Sn[0], Sn[1], Sr[0], Sr[1]);
+    else s_nop_result2(Sn[0], Sn[1]);
 
     // ---- mask + online softmax (log2 domain) --------------------------------
     // Tile-wide visibility: a tile every row of the workgroup sees in full
@@ -711,6 +843,8 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       full = page_ok && (unit + 1) * kKeys <= sk - (a.causal ? a.s_q - 1 : 0);
       limit = page_ok ? row_len - unit * kKeys : 0;
     }
+    const float cn = qk_scale * a.sm_log2;
+    f32x16 S[2];
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -721,13 +855,41 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         bool valid;
         if constexpr (SPARSE) valid = (smask >> key) & 1ull;
         else valid = key < limit;
-        const float zs = S[kb][r] * a.sm_log2;
+        float zs;
+        if constexpr (kSepRope) zs = fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2);
+        else if constexpr (ROPE > 0) zs = Sn[kb][r] * a.sm_log2;   // bf16: scaled already
+        else zs = Sn[kb][r] * cn;
         const float z = (full || valid) ? zs : -INFINITY;
         S[kb][r] = z;
         mx = fmaxf(mx, z);
       }
     }
     mx = pair_max(mx);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // The first V^T fragments of the P.V products are read now, so they are
+    // in registers when the exponentials are done (issued after the row-max
+    // exchange, whose own LDS access would otherwise wait for them).
+    constexpr int PDV = DOT == DOT_FP8 ? 3 : 2;
+    i32x8 vr[PDV];
+    auto vfrag = [&](int blk) -> i32x8 {
+      i32x8 av;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const i32x2 v = vt_bytes<GATHER_V>(nope, lane, blk, u, lb.vt[blk & 7]);
+        av[2 * u] = v.x;
+        av[2 * u + 1] = v.y;
+      }
+      return av;
+    };
+    // (bf16 dots: no early reads; their query fragments leave too few
+    // registers to hold V^T fragments across the softmax.)
+    if constexpr (DOT == DOT_FP8) {
+#pragma unroll
+      for (int blk = 0; blk < PDV; ++blk) vr[blk] = vfrag(blk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     const bool raise = mx > m_run + Soft<DOT>::tau;
     if (__ballot(raise)) {
       const float m_new = raise ? mx : m_run;
@@ -735,20 +897,20 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       l_run *= alpha;
       if (__ballot(raise && m_run != -INFINITY)) {
         // The previous tile's P.V MFMAs finished before this tile's S^T
-        // results were read (one in-order MFMA pipeline, s_nop_result).
+        // results were read (one in-order MFMA pipeline, s_nop_result4).
 #pragma unroll
         for (int blk = 0; blk < 16; ++blk) scale_agpr_acc(O[blk], alpha);
         asm volatile("s_nop 4" ::);
       }
       m_run = m_new;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT>::ps_log2;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(S[kb][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(S[kb][r] - m_exp);
         S[kb][r] = p;
         psum += p;
       }
@@ -757,30 +919,18 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
 
     // ---- O^T += V^T P^T ---------------------------------------------------------
     if constexpr (DOT == DOT_FP8) {
-      constexpr float ps = Soft<DOT>::pscale;
       i32x8 pb;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int kb = q >> 2, r0 = 4 * (q & 3);
-        pb[q] = f32x4_to_fp8x4(S[kb][r0] * ps, S[kb][r0 + 1] * ps, S[kb][r0 + 2] * ps, S[kb][r0 + 3] * ps);
+        pb[q] = f32x4_to_fp8x4(S[kb][r0], S[kb][r0 + 1], S[kb][r0 + 2], S[kb][r0 + 3]);
       }
-      auto vfrag = [&](int blk) -> i32x8 {
-        i32x8 av;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const i32x2 v = vt_bytes<GATHER_V>(nope, lane, blk, u, lb.vt);
-          av[2 * u] = v.x;
-          av[2 * u + 1] = v.y;
-        }
-        return av;
-      };
-      i32x8 nxt = vfrag(0);
-      asm volatile("s_nop 4" ::);   // pb was just written by VALU
 #pragma unroll
       for (int blk = 0; blk < 16; ++blk) {
-        const i32x8 cur = nxt;
-        if (blk + 1 < 16) nxt = vfrag(blk + 1);
-        mfma_fp8_32x32x64_acc(O[blk], cur, pb);
+        const i32x8 cur = vr[blk % PDV];
+        if (blk + PDV < 16) vr[blk % PDV] = vfrag(blk + PDV);
+        if (blk == 0) mfma_fp8_32x32x64_acc_after_valu(O[blk], cur, pb);   // pb was just written by VALU
+        else mfma_fp8_32x32x64_acc(O[blk], cur, pb);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -794,13 +944,14 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         pb[u] = __builtin_bit_cast(bf16x8, w);
       }
 #pragma unroll
-      for (int blk = 0; blk < 16; ++blk) {
-        i32x2 v[4];
+      for (int blk = 0; blk < PDV; ++blk) vr[blk] = vfrag(blk);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = vt_bytes<GATHER_V>(nope, lane, blk, u, lb.vt);
+      for (int blk = 0; blk < 16; ++blk) {
+        const i32x8 cur = vr[blk % PDV];
+        if (blk + PDV < 16) vr[blk % PDV] = vfrag(blk + PDV);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const i32x2 lo = fp8x4_to_bf16x4(v[u].x), hi = fp8x4_to_bf16x4(v[u].y);
+          const i32x2 lo = fp8x4_to_bf16x4(cur[2 * u]), hi = fp8x4_to_bf16x4(cur[2 * u + 1]);
           const bf16x8 av = __builtin_bit_cast(bf16x8, i32x4{lo.x, lo.y, hi.x, hi.y});
           mfma_bf16_32x32x16_acc(O[blk], av, pb[u]);
         }
@@ -809,7 +960,6 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     page_cur = page_next;
     page_next = page_next2;
-    page_next2 = page_after;
     row_cur = row_next;
     buf = buf_next;
   }
@@ -823,10 +973,11 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   // ---- epilogue -----------------------------------------------------------------
   // O^T register r of block blk is dv 32*blk + 8*(r/4) + 4*h + r%4 of row n.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float vs = *v_scale;
   const bool nonempty = l_tot > 0.f;
-  const float inv = nonempty ? vs / (Soft<DOT>::pscale * l_tot) : 0.f;
-  const float lse2 = nonempty ? m_run + log2f(l_tot) : -INFINITY;
+  // splits == 1: the output, scaled by v_scale; else the partials, normalized
+  // by the row sum only (fp16, |value| <= 448; the combine applies v_scale)
+  const float inv = nonempty ? (a.splits == 1 ? *v_scale : 1.f) / l_tot : 0.f;
+  const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
 
   if (a.splits == 1) {
     if (!row_ok) return;
@@ -844,72 +995,577 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     if (h == 0) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
   } else {
-    // partials in the accumulator's own register layout (coalesced 64-byte
-    // stores per lane); the combine kernel reads the same layout.
+    // partials in the accumulator's own register layout (two 16-byte stores
+    // per lane and block); the combine kernel reads the same layout.
     const long frag = ((long)s * a.groups + g) * a.row_blocks + rb;
-    float* po = part_o + frag * (16 * 64 * 16);
+    uint16_t* po = part_o + frag * (16 * 64 * 16);
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
-      float4* dst = reinterpret_cast<float4*>(po + (blk * 64 + lane) * 16);
+      i32x4* dst = reinterpret_cast<i32x4*>(po + (blk * 64 + lane) * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dst[j] = make_float4(O[blk][4 * j] * inv, O[blk][4 * j + 1] * inv,
-                             O[blk][4 * j + 2] * inv, O[blk][4 * j + 3] * inv);
+      for (int j = 0; j < 2; ++j) {
+        i32x4 w;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d] = (int)half2_bits(O[blk][8 * j + 2 * d] * inv, O[blk][8 * j + 2 * d + 1] * inv);
+        dst[j] = w;
+      }
     }
     if (h == 0) part_lse[frag * 32 + n] = lse2;
   }
 }
 
-// Split combine (InfiniCore PR #1568, split-kv commit; empty partials carry
-// lse = -inf and weight 0, so an all-empty row gives zeros and lse = -inf).
-// One workgroup per (group, 32-row block); thread (blk, lane) merges the 16
-// accumulator values that lane held for dv block blk in every split.
-__global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims a) {
-  const int g = blockIdx.x / a.row_blocks;
-  const int rb = blockIdx.x % a.row_blocks;
-  for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
-    const int blk = idx >> 6, lane = idx & 63;
-    const int n = lane & 31, h = lane >> 5;
-    const int row = rb * 32 + n;
-    if (row >= a.rows) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-      M = fmaxf(M, part_lse[(((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n]);
-    float acc[16];
+// LDS past the KV ring: what the waves exchange between the S^T products
+// (one 32-row block per wave) and the P.V products (one slice of dv per wave,
+// all row blocks), double-buffered by tile parity:
+//  * P^T operands of a tile, 2 KiB per row block, stored as two 16-byte
+//    halves per lane (lane-contiguous, so conflict free);
+//  * per-row rescale factors and one flag per row block saying whether any
+//    of its rows raised its running max (and so carries factors);
+//  * at the end, the per-row output scale 1 / l.
+template <int NW>
+struct Xchg {
+  static constexpr int p_bytes = NW * 2048;
+  static constexpr int alpha_bytes = NW * 32 * 4;
+  static constexpr int flag_off = 2 * p_bytes + 2 * alpha_bytes;   // 2 x 4 ints
+  static constexpr int fin_off = flag_off + 32;
+  static constexpr int bytes = fin_off + NW * 32 * 4;
+};
+
+// fp8-dot decode with the P.V products split over the waves by dv: wave w
+// multiplies the dv slice w of V^T with the P^T of every row block of the
+// workgroup, so each wave reads 1/NW of V from LDS instead of all of it (the
+// transposing V reads are the costliest LDS traffic of a tile). The S^T
+// products and the softmax stay with the wave that owns the row block; P^T
+// and the rescale factors cross through LDS, one tile behind.
+template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(1, 1)))
+void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
+  static_assert(DOT == DOT_FP8, "the dv-split kernel is for fp8 dots");
+  constexpr int D = kNope + ROPE;               // q row length
+  constexpr int kJ = 16 / NW;                   // 32-wide dv blocks per wave in P.V
+  using X = Xchg<NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + X::bytes];
+  uint8_t* const lds = lds_;
+  uint8_t* const xp = lds + Tile<ROPE>::lds_bytes;
+  float* const xalpha = reinterpret_cast<float*>(xp + 2 * X::p_bytes);
+  int* const xflag = reinterpret_cast<int*>(xp + X::flag_off);
+  float* const xfin = reinterpret_cast<float*>(xp + X::fin_off);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 31, h = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int rg = bid % a.row_groups;
+  bid /= a.row_groups;
+  const int s = bid % a.splits;
+  const int g = bid / a.splits;
+
+  const int b = SPARSE ? g / a.s_q : g;
+  int sk = seq_lens[b];
+  sk = max(0, min(sk, a.max_pages * kKeys));
+  const int units = SPARSE ? (a.topk + kKeys - 1) / kKeys : (sk + kKeys - 1) / kKeys;
+  const int u0 = (int)((long)s * units / a.splits);
+  const int u1 = (int)((long)(s + 1) * units / a.splits);
+  const int ntiles = u1 - u0;
+
+  const int rb = rg * NW + wave;              // row block of this wave's S^T products
+  const bool wave_active = rb < a.row_blocks;
+  const int row = rb * 32 + n;
+  const bool row_ok = row < a.rows;
+  int row_len = 0;                            // dense: keys this row may see
+  if constexpr (!SPARSE) {
+    const int i = row / a.h_q;
+    row_len = a.causal ? sk - (a.s_q - 1 - i) : sk;
+    if (!row_ok) row_len = 0;
+  }
+  const long qrow_idx = (long)g * a.rows + row;
+  const uint16_t* qrow = q + qrow_idx * D;
+
+  const int32_t* bt_row = block_table + (long)b * a.max_pages;
+  const int32_t* idx_row = SPARSE ? indices + (long)g * a.topk : nullptr;
+  constexpr long RB = kNope + 2 * ROPE;
+
+  // Cache row (page * 64 + slot) of sparse entry `e`, or -1 when skipped.
+  auto sparse_row = [&](int e) -> int {
+    int cr = -1;
+    if (e < a.topk) {
+      const int j = idx_row[e];
+      if (j >= 0 && j < sk) {
+        const int page = bt_row[j / kKeys];
+        if (page >= 0 && page < a.num_pages) cr = page * kKeys + (j % kKeys);
+      }
+    }
+    return cr;
+  };
+  // Dense: one page per tile. Inside the tile loop page ids come from a
+  // register holding 64 of them (lane i: tile 64c + i of the split), read with
+  // v_readlane: a scalar load there would share the counter of the LDS
+  // fragment reads and, completing out of order, force them to full waits.
+  auto page_of = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  auto page_of_lane = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  int pages_v = -1;
+  auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
+  auto issue_dense = [&](int unit, int page, int bufi) {
+    const bool ok = page_valid(page);
+    const int valid = ok ? min(kKeys, sk - unit * kKeys) : 0;
+    issue_dense_tile<ROPE, NW>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, lane, wave);
+  };
+
+  // Tiles are loaded one ahead: tile k+1 lands while tile k computes.
+  int page_cur = -1, page_next = -1;          // dense
+  int row_cur = -1, row_next = -1;            // sparse: this lane's tile row
+  if (ntiles > 0) {
+    if constexpr (SPARSE) {
+      row_cur = sparse_row(u0 * kKeys + lane);
+      issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
+    } else {
+      page_cur = page_of(u0);
+      issue_dense(u0, page_cur, 0);
+    }
+  }
+
+  // The first iteration's P.V step (for the non-existent tile -1) runs on
+  // zeros: P^T of parity 1 and the V region of ring buffer 2 (which tile 2
+  // only overwrites after the next barrier), and no rescale flags.
+  {
+    const int t = threadIdx.x;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    float W = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const long frag = ((long)s * a.groups + g) * a.row_blocks + rb;
-        const float ls = part_lse[frag * 32 + n];
-        if (ls == -INFINITY) continue;
-        const float w = exp2f(ls - M);
-        W += w;
-        const float4* src = reinterpret_cast<const float4*>(part_o + frag * (16 * 64 * 16) + (blk * 64 + lane) * 16);
+    for (int i = 0; i < kNopeRegion / (NW * 1024); ++i)
+      *reinterpret_cast<i32x4*>(lds + 2 * kNopeRegion + (i * NW * 64 + t) * 16) = i32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 v = src[j];
-          acc[4 * j] += w * v.x;
-          acc[4 * j + 1] += w * v.y;
-          acc[4 * j + 2] += w * v.z;
-          acc[4 * j + 3] += w * v.w;
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<i32x4*>(xp + X::p_bytes + (i * NW * 64 + t) * 16) = i32x4{0, 0, 0, 0};
+    if (t < 8) xflag[t] = 0;
+  }
+
+  // Q fragments (B operand of S^T = K Q^T).
+  i32x8 qn[DOT == DOT_FP8 ? 8 : 1];
+  bf16x8 qb[DOT == DOT_BF16 ? 32 : 1];
+  bf16x8 qr[ROPE > 0 ? 4 : 1];
+  float qk_scale;   // q_scale * k_scale, applied to the nope products
+  {
+    const float ks = *k_scale;
+    if constexpr (DOT == DOT_FP8) {
+      int e;
+      stage_q_fp8(qrow, row_ok && wave_active, h, qn, e);
+      qk_scale = ldexpf(ks, e);
+    } else {
+      qk_scale = ks;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int d0 = 32 * (u >> 1) + 16 * h + 8 * (u & 1);
+        i32x4 v = row_ok ? *reinterpret_cast<const i32x4*>(qrow + d0) : i32x4{0, 0, 0, 0};
+        qb[u] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        i32x4 v = row_ok ? *reinterpret_cast<const i32x4*>(qrow + kNope + 16 * t + 8 * h)
+                         : i32x4{0, 0, 0, 0};
+        qr[t] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+
+  // All query loads are complete before the tile loop: the tile copies are
+  // inline asm the compiler does not count, and without this it would wait
+  // for every outstanding copy before the first use of a query register in
+  // each tile.
+  if constexpr (!SPARSE) pages_v = page_of_lane(u0 + lane);
+  wait_vmcnt<0>();
+  asm volatile("" : "+v"(pages_v));   // loaded before the loop, not inside it
+
+  const LdsBases lb(lane);
+  // V^T lane bases of this wave's dv blocks (block wave * kJ + j, j < kJ)
+  int vtw[kJ < 8 ? kJ : 8];
+#pragma unroll
+  for (int j = 0; j < (kJ < 8 ? kJ : 8); ++j) vtw[j] = vt_lane_base(lane, (wave * kJ + j) & 7);
+
+  // O^T accumulators: block j * NW + r holds dv 32 * (wave * kJ + j) .. +31 of
+  // the workgroup's row block r.
+  f32x16 O[16];
+#pragma unroll
+  for (int blk = 0; blk < 16; ++blk) O[blk] = f32x16{};
+  float m_run = -INFINITY;   // max used for the exponentials (log2 domain)
+  float l_run = 0.f;         // this lane's share of the running sum
+
+  // Iteration k computes S^T and the softmax of tile k (k < ntiles) and the
+  // P.V products of tile k-1, whose P^T the waves exchanged through LDS; the
+  // last iteration only finishes tile ntiles-1.
+  int buf = 0, bufp = 2;     // ring buffers of tiles k and k-1
+  for (int k = 0; k <= ntiles; ++k) {
+    const int par = k & 1;
+    const bool live = k < ntiles;
+    if (live) wait_vmcnt<0>();   // tile k has landed
+    __syncthreads();             // ... for every wave; P^T, flags of tile k-1 are visible
+    const int buf_next = buf == kBufs - 1 ? 0 : buf + 1;
+    const uint8_t* spread_page = nullptr;   // dense full tile k+1, copied during S^T
+    auto t1u = [&](int t) { return u0 + t; };
+    if (k + 1 < ntiles) {
+      if constexpr (SPARSE) {
+        row_next = sparse_row((u0 + k + 1) * kKeys + lane);
+        issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
+      } else {
+        const int t1 = k + 1;
+        if ((t1 & 63) == 0) {   // next 64 page ids (tile loops longer than 64 tiles)
+          pages_v = page_of_lane(u0 + t1 + lane);
+          wait_vmcnt<0>();
+        }
+        page_next = __builtin_amdgcn_readlane(pages_v, t1 & 63);
+        // A full tile's copies are spread over the S^T loop below: issued in
+        // one burst they stall the wave (the CU's vector memory path takes a
+        // 1 KiB copy per ~16 cycles and all waves issue at once) while the
+        // matrix core idles. Partial or missing pages are issued here.
+        const bool ok = page_valid(page_next);
+        if (ok && sk - t1u(t1) * kKeys >= kKeys) {
+          spread_page = kv + (long)page_next * kKeys * RB;
+        } else {
+          issue_dense(u0 + t1, page_next, buf_next);
         }
       }
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    const long qrow_idx = (long)g * a.rows + row;
-    uint16_t* orow = out + qrow_idx * kNope;
+
+    // flags of tile k-1 (read now, used after the S^T products)
+    const i32x4 fl = *reinterpret_cast<const i32x4*>(xflag + 4 * (par ^ 1));
+
+    const uint8_t* nope = lds + buf * kNopeRegion;
+    const uint8_t* rope = lds + kRopeBase + buf * kRopeRegion;
+    const uint8_t* vnope = lds + bufp * kNopeRegion;            // V of tile k-1
+    const uint8_t* pprev = xp + (par ^ 1) * X::p_bytes;         // P^T of tile k-1
+    const int unit = u0 + k;
+
+    // P.V operands of tile k-1: P^T of every row block, and a ring of V^T
+    // fragments (one per 32-wide dv block, each used by NW products).
+    constexpr int PDV = NW == 4 ? 2 : 3;
+    i32x8 pt[NW];
+    i32x8 vr[PDV];
+    auto vfrag = [&](int j) -> i32x8 {
+      const int blk = wave * kJ + j;
+      i32x8 av;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int dv = 32 * blk + 8 * j + 4 * h;
-      uint2 w;
-      w.x = bf16x2_bits(acc[4 * j] * inv, acc[4 * j + 1] * inv);
-      w.y = bf16x2_bits(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + dv) = w;
+      for (int u = 0; u < 4; ++u) {
+        const i32x2 v = vt_bytes<GATHER_V>(vnope, lane, blk, u, vtw[j & 7]);
+        av[2 * u] = v.x;
+        av[2 * u + 1] = v.y;
+      }
+      return av;
+    };
+    auto load_pv_operands = [&]() {
+#pragma unroll
+      for (int r = 0; r < NW; ++r) {
+        const i32x4 lo = lds_ld16(pprev, r * 2048 + lane * 16);
+        const i32x4 hi = lds_ld16(pprev, r * 2048 + 1024 + lane * 16);
+        pt[r] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < PDV && j < kJ; ++j) vr[j] = vfrag(j);
+    };
+
+    // ---- S^T = K Q^T -------------------------------------------------------
+    // The fragment reads of a tile run through a ring several items deep, so
+    // about ten LDS reads are in flight while the MFMAs consume earlier ones
+    // (one wave per SIMD: nothing else hides the LDS latency). Items alternate
+    // between the two 32-key blocks, so consecutive MFMAs are independent. The
+    // rope products have accumulators of their own, since q_scale * k_scale
+    // applies to the nope products only; both are combined in the softmax.
+    // Scheduling barriers keep the compiler from hoisting the whole tile's
+    // fragment reads (which would need up to 160 more registers). The P.V
+    // operands of tile k-1 are read as the ring drains. On the extra last
+    // iteration these products run on stale LDS data that the mask discards.
+    f32x16 Sn[2], Sr[2];
+    if constexpr (ROPE == 0) Sr[0] = Sr[1] = f32x16{};
+    {
+      constexpr int NN = 16, NI = NN + (ROPE > 0 ? 8 : 0), PD = 5;
+      i32x4 rl[PD], rh[PD];
+      auto load = [&](int f) {
+        const int slot = f % PD, kb = f & 1;
+        if (f < NN) {
+          const int t = f >> 1;
+          const int c = 32 * kb * kNope + 256 * (t >> 2);
+          rl[slot] = lds_ld16(nope, lb.k8[t & 3][0] + c);
+          rh[slot] = lds_ld16(nope, lb.k8[t & 3][1] + c);
+        } else {
+          rl[slot] = lds_ld16(rope, lb.rp[(f - NN) >> 1] + 32 * kb * 128);
+        }
+      };
+#pragma unroll
+      for (int f = 0; f < PD; ++f) load(f);
+#pragma unroll
+      for (int f = 0; f < NI; ++f) {
+        const int slot = f % PD, kb = f & 1;
+        const i32x4 lo = rl[slot], hi = rh[slot];
+        if (f + PD < NI) load(f + PD);
+        if (f + PD == NI) load_pv_operands();
+        if constexpr (!SPARSE) {
+          constexpr int LPW = Tile<ROPE>::template loads_per_wave<NW>();
+          if (spread_page != nullptr) {
+#pragma unroll
+            for (int jj = f * LPW / NI; jj < (f + 1) * LPW / NI; ++jj)
+              issue_dense_load<ROPE, NW>(lds, buf_next, spread_page, jj, wave);
+          }
+        }
+        if (f < NN) {
+          const i32x8 kf = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          if (f < 2) mfma_fp8_32x32x64_first(Sn[kb], kf, qn[f >> 1]);
+          else mfma_fp8_32x32x64(Sn[kb], kf, qn[f >> 1]);
+        } else {
+          const bf16x8 kr = __builtin_bit_cast(bf16x8, lo);
+          if (f < NN + 2) mfma_bf16_32x32x16_first(Sr[kb], kr, qr[(f - NN) >> 1]);
+          else mfma_bf16_32x32x16(Sr[kb], kr, qr[(f - NN) >> 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (blk == 0 && h == 0) lse[qrow_idx] = (W > 0.f) ? (M + log2f(W)) * kLn2 : -INFINITY;
+    if constexpr (ROPE > 0) s_nop_result4(Sn[0], Sn[1], Sr[0], Sr[1]);
+    else s_nop_result2(Sn[0], Sn[1]);
+
+    // ---- rescale O for the rows whose max tile k-1 raised (rare) ---------------
+    // (before the P.V products of tile k-1; the previous iteration's P.V
+    // MFMAs, the last writers of O, completed long before)
+    if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]),
+                     "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]),
+                     "+a"(O[14]), "+a"(O[15]));
+      const float* al = xalpha + (par ^ 1) * (NW * 32);
+#pragma unroll
+      for (int r = 0; r < NW; ++r) {
+        if (__builtin_amdgcn_readfirstlane(fl[r])) {   // only row blocks that raised
+          const float f = al[r * 32 + n];
+#pragma unroll
+          for (int j = 0; j < kJ; ++j) scale_agpr_acc(O[j * NW + r], f);
+        }
+      }
+      asm volatile("s_nop 4" ::);
+    }
+
+
+    // ---- softmax of tile k, interleaved with the P.V products of tile k-1 ----
+    // The 16 P.V MFMAs do not depend on the softmax, so its VALU work is cut
+    // into slices issued between them; a slice runs while the matrix core
+    // works on the MFMA before it. Slices 0-3: mask, scale and row max; 4: the
+    // max goes to the other lane half (lanes l and l ^ 32 share a row); 6: the
+    // lazy raise; 7-14: exponentials; 15: P^T packing, P^T and flags to LDS.
+    bool full;
+    int limit = 0;    // dense: keys of this tile this lane's row may see
+    unsigned long long smask = 0;
+    if constexpr (SPARSE) {
+      smask = live ? __ballot(row_cur >= 0) : 0ull;
+      full = smask == ~0ull;
+    } else {
+      const bool page_ok = live && page_valid(page_cur);
+      full = page_ok && (unit + 1) * kKeys <= sk - (a.causal ? a.s_q - 1 : 0);
+      limit = page_ok ? row_len - unit * kKeys : 0;
+    }
+    const float cn = qk_scale * a.sm_log2;
+    f32x16 S[2];
+    float mx = -INFINITY;
+    int mx_other = 0;
+    bool flagged = false;
+    float psum = 0.f, m_exp = 0.f;
+    i32x8 pb;
+    auto slice = [&](int i) {
+      if (i < 4) {
+        const int kb = i >> 1, r0 = 8 * (i & 1);
+        if (full) {   // every key of the tile is visible to every row
+#pragma unroll
+          for (int r = r0; r < r0 + 8; ++r) {
+            const float z = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
+            S[kb][r] = z;
+            mx = fmaxf(mx, z);
+          }
+        } else {
+#pragma unroll
+          for (int r = r0; r < r0 + 8; ++r) {
+            const int j = r >> 2;
+            const int key = 32 * kb + 8 * j + 4 * ((j + h) & 1) + (r & 3);
+            bool valid;
+            if constexpr (SPARSE) valid = (smask >> key) & 1ull;
+            else valid = key < limit;
+            const float zs = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
+            const float z = valid ? zs : -INFINITY;
+            S[kb][r] = z;
+            mx = fmaxf(mx, z);
+          }
+        }
+      } else if (i == 4) {
+        mx_other = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(mx));
+      } else if (i == 6) {
+        mx = fmaxf(mx, __int_as_float(mx_other));
+        const bool raise = mx > m_run + Soft<DOT>::tau;
+        if (__ballot(raise)) {
+          const float m_new = raise ? mx : m_run;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+          l_run *= alpha;
+          // O needs rescaling only where a finite max was raised
+          flagged = __ballot(raise && m_run != -INFINITY) != 0ull;
+          if (flagged && h == 0) {
+            int ln;   // lane id recomputed here (a kept copy gets spilled)
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            xalpha[par * (NW * 32) + wave * 32 + (ln & 31)] = alpha;
+          }
+          m_run = m_new;
+        }
+        m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT>::ps_log2;
+      } else if (i >= 7 && i < 15) {
+        const int kb = (i - 7) >> 2, r0 = 4 * ((i - 7) & 3);
+#pragma unroll
+        for (int r = r0; r < r0 + 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(S[kb][r] - m_exp);
+          S[kb][r] = p;
+          psum += p;
+        }
+      } else if (i == 15) {
+        l_run += psum;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int kb = q >> 2, r0 = 4 * (q & 3);
+          pb[q] = f32x4_to_fp8x4(S[kb][r0], S[kb][r0 + 1], S[kb][r0 + 2], S[kb][r0 + 3]);
+        }
+        uint8_t* pdst = xp + par * X::p_bytes + wave * 2048 + lane * 16;
+        *reinterpret_cast<i32x4*>(pdst) = i32x4{pb[0], pb[1], pb[2], pb[3]};
+        *reinterpret_cast<i32x4*>(pdst + 1024) = i32x4{pb[4], pb[5], pb[6], pb[7]};
+        if (lane == 0) xflag[4 * par + wave] = flagged ? 1 : 0;
+      }
+    };
+
+    // O^T += V^T P^T for tile k-1: dv block j of this wave's kJ times row
+    // block r, 16 MFMAs, with a softmax slice after each.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = i / NW, r = i % NW;
+      if (r == 0 && j > 0 && j + PDV - 1 < kJ) vr[(j + PDV - 1) % PDV] = vfrag(j + PDV - 1);
+      mfma_fp8_32x32x64_acc(O[i], vr[j % PDV], pt[r]);
+      __builtin_amdgcn_sched_barrier(0);
+      slice(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    page_cur = page_next;
+    row_cur = row_next;
+    bufp = buf;
+    buf = buf_next;
   }
+
+  // ---- epilogue -----------------------------------------------------------------
+  // The last P.V MFMAs have completed before VALU reads O.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]), "+a"(O[7]),
+                 "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const bool nonempty = l_tot > 0.f;
+  // splits == 1: output scale v_scale / l; else the partials' 1 / l (fp16
+  // partials, |value| <= 448; the combine applies v_scale)
+  if (h == 0) xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? *v_scale : 1.f) / l_tot : 0.f;
+  if (wave_active && h == 0) {
+    const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
+    if (a.splits == 1) {
+      if (row_ok) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
+    } else {
+      part_lse[(((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n] = lse2;
+    }
+  }
+  __syncthreads();
+  // O^T register e of block j * NW + r: dv 32 * (wave * kJ + j) + 8 * (e / 4) +
+  // 4 * h + e % 4, row 32 * (row block) + n.
+#pragma unroll
+  for (int r = 0; r < NW; ++r) {
+    const int rbr = rg * NW + r;
+    if (rbr >= a.row_blocks) break;
+    const float inv = xfin[r * 32 + n];
+    const int rowr = rbr * 32 + n;
+    if (a.splits == 1) {
+      if (rowr < a.rows) {
+        uint16_t* orow = out + ((long)g * a.rows + rowr) * kNope;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int dv = 32 * (wave * kJ + j) + 8 * e4 + 4 * h;
+            const f32x16& o = O[j * NW + r];
+            uint2 w;
+            w.x = bf16x2_bits(o[4 * e4] * inv, o[4 * e4 + 1] * inv);
+            w.y = bf16x2_bits(o[4 * e4 + 2] * inv, o[4 * e4 + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + dv) = w;
+          }
+        }
+      }
+    } else {
+      // partials in the accumulator's own register layout (two 16-byte
+      // stores per lane and block); the combine kernel reads the same layout.
+      const long frag = ((long)s * a.groups + g) * a.row_blocks + rbr;
+      uint16_t* po = part_o + frag * (16 * 64 * 16);
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const f32x16& o = O[j * NW + r];
+        i32x4* dst = reinterpret_cast<i32x4*>(po + ((wave * kJ + j) * 64 + lane) * 16);
+#pragma unroll
+        for (int e8 = 0; e8 < 2; ++e8) {
+          i32x4 w;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) w[d] = (int)half2_bits(o[8 * e8 + 2 * d] * inv, o[8 * e8 + 2 * d + 1] * inv);
+          dst[e8] = w;
+        }
+      }
+    }
+  }
+}
+
+// Split combine (InfiniCore PR #1568, split-kv commit; empty partials carry
+// lse = -inf and weight 0, so an all-empty row gives zeros and lse = -inf).
+// Four workgroups per (group, 32-row block); thread (blk, lane) merges the 16
+// accumulator values that lane held for dv block blk in every split. The
+// partials are normalized by their own row sums; v_scale is applied here.
+__global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims a) {
+  const int gr = blockIdx.x >> 2;
+  const int g = gr / a.row_blocks;
+  const int rb = gr % a.row_blocks;
+  const int blk = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const int row = rb * 32 + n;
+  if (row >= a.rows) return;
+  const long frag0 = (long)g * a.row_blocks + rb;          // split s: frag0 + s * groups * row_blocks
+  const long fstride = (long)a.groups * a.row_blocks;
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, part_lse[(frag0 + sp * fstride) * 32 + n]);
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  float W = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const long frag = frag0 + sp * fstride;
+      const float ls = part_lse[frag * 32 + n];
+      const float w = ls == -INFINITY ? 0.f : exp2f(ls - M);
+      W += w;
+      const i32x4* src = reinterpret_cast<const i32x4*>(part_o + frag * (16 * 64 * 16) + (blk * 64 + lane) * 16);
+      const i32x4 v0 = src[0], v1 = src[1];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] += w * half_lo((unsigned)v0[d]);
+        acc[2 * d + 1] += w * half_hi((unsigned)v0[d]);
+        acc[8 + 2 * d] += w * half_lo((unsigned)v1[d]);
+        acc[8 + 2 * d + 1] += w * half_hi((unsigned)v1[d]);
+      }
+    }
+  }
+  const float inv = W > 0.f ? *v_scale / W : 0.f;
+  const long qrow_idx = (long)g * a.rows + row;
+  uint16_t* orow = out + qrow_idx * kNope;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int dv = 32 * blk + 8 * j + 4 * h;
+    uint2 w;
+    w.x = bf16x2_bits(acc[4 * j] * inv, acc[4 * j + 1] * inv);
+    w.y = bf16x2_bits(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+    *reinterpret_cast<uint2*>(orow + dv) = w;
+  }
+  if (blk == 0 && h == 0) lse[qrow_idx] = (W > 0.f) ? (M + log2f(W)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -966,7 +1622,7 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(const uint8_t* kv, co
   uint8_t* dst = dense_out + ((long)b * max_pages + unit) * kKeys * RB;
   for (int idx = threadIdx.x; idx < kKeys * (RB / 16); idx += 256) {
     const int r = idx / (RB / 16), c = idx % (RB / 16);
-    const int off = c < 32 ? r * kNope + (swz(r, c) << 4) : kRopeBase + r * 128 + (swz(r, c - 32) << 4);
+    const int off = c < 32 ? r * kNope + (swz(r, c) << 4) : kRopeBase + r * 128 + (swz_rope(r, c - 32) << 4);
     *reinterpret_cast<i32x4*>(dst + r * RB + c * 16) = lds_ld16(lds, off);
   }
 }
@@ -986,7 +1642,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* src, long
 
 size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks) {
   const size_t frags = (size_t)splits * groups * row_blocks;
-  return frags * (16 * 64 * 16 * sizeof(float)) + frags * 32 * sizeof(float);
+  return frags * (16 * 64 * 16 * sizeof(uint16_t)) + frags * 32 * sizeof(float);
 }
 
 // Waves per workgroup: one per 32-row block, up to 4 (1, 2 or 4 so that the
@@ -1007,22 +1663,38 @@ static KDims make_dims(const DecodeLaunch& d) {
 #define MLA_PTR_ARGS(d) \
   d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
 
-template <int DOT, int ROPE, bool SPARSE, bool GV>
+template <int DOT, int ROPE, bool SPARSE, bool GV, bool XCH>
 static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   const int nw = waves_per_group(d.row_blocks);
   const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
+#define MLA_LAUNCH(NWV)                                                                                  \
+  if constexpr (XCH)                                                                                     \
+    hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, NWV, GV>), grid, dim3(64 * NWV), 0, st,      \
+                       MLA_PTR_ARGS(d), a);                                                              \
+  else                                                                                                   \
+    hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, NWV, GV>), grid, dim3(64 * NWV), 0, st, \
+                       MLA_PTR_ARGS(d), a);
   switch (nw) {
-    case 1: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 1, GV>), grid, dim3(64), 0, st, MLA_PTR_ARGS(d), a); break;
-    case 2: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 2, GV>), grid, dim3(128), 0, st, MLA_PTR_ARGS(d), a); break;
-    default: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 4, GV>), grid, dim3(256), 0, st, MLA_PTR_ARGS(d), a); break;
+    case 1: MLA_LAUNCH(1) break;
+    case 2: MLA_LAUNCH(2) break;
+    default: MLA_LAUNCH(4) break;
   }
+#undef MLA_LAUNCH
   return hipGetLastError();
 }
 
+// fp8 dots run the dv-split kernel (or, on request, the row-block one);
+// bf16 dots the row-block kernel.
 template <int DOT, int ROPE, bool SPARSE>
 static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
-  return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true>(d, a, st)
-                    : launch_nw<DOT, ROPE, SPARSE, false>(d, a, st);
+  if constexpr (DOT == DOT_FP8) {
+    if (d.rows_kernel) return launch_nw<DOT, ROPE, SPARSE, false, false>(d, a, st);
+    return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, true>(d, a, st)
+                      : launch_nw<DOT, ROPE, SPARSE, false, true>(d, a, st);
+  } else {
+    return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, false>(d, a, st)
+                      : launch_nw<DOT, ROPE, SPARSE, false, false>(d, a, st);
+  }
 }
 
 template <int DOT, int ROPE>
@@ -1047,7 +1719,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t st) {
 
 hipError_t launch_combine(const DecodeLaunch& d, hipStream_t st) {
   const KDims a = make_dims(d);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(a.groups * a.row_blocks)), dim3(256), 0, st,
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(a.groups * a.row_blocks * 4)), dim3(256), 0, st,
                      MLA_PTR_ARGS(d), a);
   return hipGetLastError();
 }

@@ -34,8 +34,10 @@
  *   bottom-right aligned (token i of s_q sees keys 0 .. seq_len - s_q + i);
  *   k_scale scales only the fp8 part of K; sparse rows take no causal mask.
  *   MLA_DOT_FP8 quantizes each query row's nope part to e4m3fn with its own
- *   power-of-two scale (the smallest 2^e with amax <= 448 * 2^e) and P to
- *   e4m3fn after multiplying it by 256; MLA_DOT_BF16 keeps Q in bf16 and
+ *   power-of-two scale (the smallest 2^e with amax <= 448 * 2^e), and P,
+ *   taken against a running row max that is only raised when a tile exceeds
+ *   it by more than 3 in log2 units (so p <= 8), to e4m3fn after scaling it
+ *   by 32 (values <= 256); MLA_DOT_BF16 keeps Q in bf16 and
  *   converts the cache bytes to bf16 exactly.
  *
  * Ownership, streams and threads: the library never allocates, frees or

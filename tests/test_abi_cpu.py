@@ -119,7 +119,7 @@ def test_workspace_size(L):
     p = good(batch=64, s_q=2, h_q=64)
     assert mla.workspace_size(p, 1) == 0
     frags = 4 * 64 * 4
-    assert mla.workspace_size(p, 4) == frags * (16 * 64 * 16 * 4 + 32 * 4)
+    assert mla.workspace_size(p, 4) == frags * (16 * 64 * 16 * 2 + 32 * 4)
     assert mla.workspace_size(good(batch=0), 4) == 0
 
 

@@ -120,3 +120,22 @@ def test_full_config(name, dot):
     w, oc, t = _case(name)
     res = gu.check(w, oc, dot, t=t)
     print(f"full {name} dot={dot}: {res}")
+
+
+@pytest.mark.parametrize("case", [("tiny", {"batch": 2, "s_q": 2, "h_q": 64, "seq_len": [700, 3], "seed": 91}),
+                                  ("tiny", {"batch": 3, "s_q": 2, "h_q": 48, "seq_len": [130, 64, 2], "seed": 92}),
+                                  ("tiny", {"batch": 2, "s_q": 1, "h_q": 16, "d_rope": 0, "seq_len": [257, 90], "seed": 93}),
+                                  ("sparse", {"batch": 2, "seq_len": 3000, "topk": 200, "seed": 94}),
+                                  ("metric", {})])
+def test_dv_split_kernel_matches_row_block_kernel(case, monkeypatch):
+    """fp8 dots: splitting P.V over the waves by dv (P^T exchanged through LDS)
+    issues the same products in the same order as the row-block kernel, so the
+    two agree bit for bit, for every split count."""
+    name, kw = case
+    w, oc, t = _case(name, **kw)
+    for splits in (1, 3, 0):
+        a = gu.run(w, t, "fp8", splits)
+        monkeypatch.setenv("MLA_FP8_ROWS_KERNEL", "1")
+        b = gu.run(w, t, "fp8", splits)
+        monkeypatch.delenv("MLA_FP8_ROWS_KERNEL")
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"splits={splits}"
