@@ -70,6 +70,26 @@ def hbm_read_probe(dev, gib=2.0, reps=5):
     return best
 
 
+PROFILE = os.path.join(ROOT, "profiles", "mla_decode_kernel.benchmark_workload.txt")
+
+
+def measured_traffic():
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary, or None when it was taken on another version of the kernel."""
+    from fp8_kv_cache_paged_amd import profile_summary
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(l.strip().split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(" "))
+    if fields.get("source_sha256") != profile_summary.source_sha256():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, budget_s):
     """The oracle (float64 NumPy, unmodified) on a bounded sample of sequences."""
     from oracle import attn
@@ -216,7 +236,7 @@ def main():
         "frac_of_measured_hbm": round(gbps / hbm_meas, 4),
         "frac_of_fp8_mfma_peak": round(tflops / (FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "kernel": "mla_decode_kernel", "kernel_us": round(kern_ms * 1e3, 2),
                      "bytes_per_launch": kern_bytes},
         "cpu_baseline": None,

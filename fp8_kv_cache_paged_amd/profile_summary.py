@@ -1,0 +1,117 @@
+"""Summarize rocprofv3 outputs of a bench.py run into a short text report.
+
+usage:
+  python -m fp8_kv_cache_paged_amd.profile_summary --stats DIR --fetch DIR --write DIR \
+      [--bench-json FILE] --command CMD ... --out profiles/<name>.txt
+
+DIR are rocprofv3 output directories (``-d DIR -o NAME --output-format csv``)
+of the same bench.py command: one ``--kernel-trace --stats`` run and two
+``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE). The HBM traffic of the split
+kernel is the per-dispatch counter value scaled by what the same counter reads
+for kernels of known size in the same run: the 2 GiB streaming read that
+bench.py times (FETCH_SIZE) and torch's 2 GiB fill before it (WRITE_SIZE).
+The report records the SHA-256 of the kernel source it was taken with;
+bench.py only reports the traffic while the source is unchanged.
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(PKG, "csrc", "mla_decode.hip")
+SPLIT_KERNEL = "mla::mla_decode_kernel<"
+STREAM_BYTES = 2 << 30          # bench.py's HBM read probe
+FILL_BYTES = 2 << 30            # torch fill of the same buffer
+
+
+def source_sha256(path=KERNEL_SOURCE):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _one(pattern):
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def kernel_stats(stats_dir):
+    rows = list(csv.DictReader(open(_one(os.path.join(stats_dir, "**", "*kernel_stats.csv")))))
+    return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["Percentage"])) for r in rows]
+
+
+def counter_by_kernel(pmc_dir, counter):
+    out = {}
+    for r in csv.DictReader(open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))):
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _match(d, needle):
+    vals = [v for k, vs in d.items() if needle in k for v in vs]
+    if not vals:
+        raise KeyError(needle)
+    return vals
+
+
+def traffic(fetch_dir, write_dir):
+    f = counter_by_kernel(fetch_dir, "FETCH_SIZE")
+    w = counter_by_kernel(write_dir, "WRITE_SIZE")
+    f_probe = _match(f, "stream_read_kernel")
+    fetch_scale = STREAM_BYTES / (sum(f_probe) / len(f_probe) * 1024.0)
+    w_fill = _match(w, "FillFunctor<unsigned char>")
+    write_scale = FILL_BYTES / (sum(w_fill) * 1024.0)   # one fill, split over launches
+    fk = _match(f, SPLIT_KERNEL)
+    wk = _match(w, SPLIT_KERNEL)
+    fetch_b = sum(fk) / len(fk) * 1024.0 * fetch_scale
+    write_b = sum(wk) / len(wk) * 1024.0 * write_scale
+    return {"fetch_scale": fetch_scale, "write_scale": write_scale, "fetch_bytes": fetch_b,
+            "write_bytes": write_b, "traffic_bytes": fetch_b + write_b, "dispatches": len(fk)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--bench-json")
+    ap.add_argument("--command", action="append", default=[], help="command lines that produced DIRs")
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+    st = kernel_stats(a.stats)
+    tr = traffic(a.fetch, a.write)
+    lines = ["# rocprofv3 summary: mla_decode_kernel (fp8 dots), benchmark workload", ""]
+    lines += ["commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):"]
+    lines += [f"  {c}" for c in a.command]
+    lines += ["", f"source_sha256: {source_sha256()}", ""]
+    lines += ["kernel stats (--kernel-trace --stats):", f"  {'calls':>6} {'avg_us':>10} {'pct':>6}  name"]
+    for name, calls, avg, pct in st[:8]:
+        lines.append(f"  {calls:>6} {avg / 1e3:>10.2f} {pct:>6.2f}  {name[:110]}")
+    lines += ["", "HBM traffic of the split kernel (--pmc FETCH_SIZE / WRITE_SIZE, per dispatch):",
+              f"  FETCH_SIZE scale {tr['fetch_scale']:.4f} (2 GiB streaming read), "
+              f"WRITE_SIZE scale {tr['write_scale']:.4f} (2 GiB fill)",
+              f"  fetch_bytes_per_launch: {tr['fetch_bytes']:.0f}",
+              f"  write_bytes_per_launch: {tr['write_bytes']:.0f}",
+              f"traffic_bytes_per_launch: {tr['traffic_bytes']:.0f}",
+              f"  dispatches averaged: {tr['dispatches']}"]
+    if a.bench_json:
+        rec = [json.loads(l) for l in open(a.bench_json) if l.strip().startswith("{")][-1]
+        rf = rec.get("roofline", {})
+        lines += ["", "bench.py line of the --kernel-trace run:",
+                  f"  ms_per_call {rec.get('ms_per_step')}, split kernel (HIP events) {rf.get('kernel_us')} us, "
+                  f"algorithmic bytes/launch {rf.get('bytes_per_launch')}, achieved {rf.get('achieved')} GB/s"]
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
