@@ -159,8 +159,12 @@ __device__ inline int swz_rope(int row, int chunk) { return chunk ^ ((row >> 1) 
 // as possibly aliasing the in-flight copy (it would then wait for all
 // outstanding loads, draining the prefetch ring); the tile loop orders the
 // copies with explicit vmcnt waits and a barrier instead.
-__device__ inline void load_lds16(const uint8_t* src, uint8_t* lds_base) {
-  const unsigned m0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_base;
+__device__ __attribute__((always_inline)) inline void load_lds16(const uint8_t* src, uint8_t* lds_base) {
+  // A generic pointer into LDS carries the LDS address in its low 32 bits
+  // (the high half is the LDS aperture). readfirstlane: the base is
+  // wave-uniform; this keeps it in a scalar register even where the compiler
+  // cannot prove that.
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(m0)
@@ -172,6 +176,18 @@ __device__ inline float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); 
 
 // Wave index within the workgroup, as a wave-uniform (scalar) value.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Workgroup i of a launch goes to XCD i % 8 (round-robin over the 8 dies,
+// each with its own L2). The logical index returned here makes consecutive
+// logical ids share a die: the splits of one query group then read its query
+// rows through one L2 instead of four. The first 8 * (n / 8) ids are permuted
+// among themselves, the rest keep their place.
+constexpr int kXcds = 8;
+__device__ inline int xcd_grouped_block(int bid, int n) {
+  const int per = n / kXcds;
+  if (bid >= per * kXcds) return bid;
+  return (bid % kXcds) * per + bid / kXcds;
+}
 
 __device__ inline i32x4 lds_ld16(const uint8_t* base, int off) {
   return *reinterpret_cast<const i32x4*>(base + off);
@@ -221,13 +237,22 @@ __device__ inline LoadOffsets<ROPE> fresh_offsets(int) {
 }
 
 // Issue the global->LDS copies of one 64-key tile into buffer `bufi`.
+// Zero 16 bytes of LDS (a lane's share of a skipped copy). The zero comes
+// from a volatile move at the store: a plain constant is kept in registers
+// across the tile loop and, under its register pressure, spilled.
+__device__ inline void lds_zero16(uint8_t* dst) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  *reinterpret_cast<i32x4*>(dst) = i32x4{z, z, z, z};
+}
+
 // Dense tiles read one page: `page_base` points at its first row and rows
 // >= `valid` are zero-filled instead of loaded (the page's slack). A full
 // tile issues exactly Tile::loads_per_wave loads per wave, which the tile
 // loop's vmcnt waits count on; a partial tile issues a data-dependent number
 // and therefore drains all outstanding loads before returning.
 template <int ROPE, int NW>
-__device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* page_base, int valid,
+__device__ __attribute__((always_inline)) inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* page_base, int valid,
                                         int lane, int wave) {
   constexpr int RB = kNope + 2 * ROPE;
   const LoadOffsets<ROPE> lo = fresh_offsets<ROPE>(lane);
@@ -252,7 +277,7 @@ __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* p
       if (row0 + 2 * jj < valid)
         load_lds16(nsrc + (unsigned)(2 * jj * RB + lo.nope_lane(jj & 7)), nope + jj * 1024);
       else
-        *reinterpret_cast<i32x4*>(nope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+        lds_zero16(nope + jj * 1024 + lane * 16);
     }
     if constexpr (ROPE > 0) {
 #pragma unroll
@@ -260,7 +285,7 @@ __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* p
         if (rrow0 + 8 * jj < valid)
           load_lds16(rsrc + (unsigned)(8 * jj * RB + lo.rope_lane[jj & 1]), rope + jj * 1024);
         else
-          *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+          lds_zero16(rope + jj * 1024 + lane * 16);
       }
     }
     wait_vmcnt<0>();
@@ -271,7 +296,7 @@ __device__ inline void issue_dense_tile(uint8_t* lds, int bufi, const uint8_t* p
 // (page * 64 + slot) that this lane resolved for tile row `lane`, or -1 for a
 // skipped entry (zero-filled).
 template <int ROPE, int NW>
-__device__ inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* kv, int mine,
+__device__ __attribute__((always_inline)) inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* kv, int mine,
                                          int lane, int wave) {
   constexpr int RB = kNope + 2 * ROPE;
   const LoadOffsets<ROPE> lo = fresh_offsets<ROPE>(lane);
@@ -285,7 +310,7 @@ __device__ inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* 
     if (cr >= 0)
       load_lds16(kv + (long)cr * RB + (lo.nope_lane(jj & 7) - (lane >> 5) * RB), nope + jj * 1024);
     else
-      *reinterpret_cast<i32x4*>(nope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+      lds_zero16(nope + jj * 1024 + lane * 16);
   }
   if constexpr (ROPE > 0) {
 #pragma unroll
@@ -294,7 +319,7 @@ __device__ inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* 
       if (cr >= 0)
         load_lds16(kv + (long)cr * RB + (lo.rope_lane[jj & 1] - (lane >> 3) * RB), rope + jj * 1024);
       else
-        *reinterpret_cast<i32x4*>(rope + jj * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+        lds_zero16(rope + jj * 1024 + lane * 16);
     }
   }
 }
@@ -523,14 +548,20 @@ struct KDims {
 // halves (lanes n and n+32). Fragment t (K = 64 dims 64t .. 64t+63) holds dims
 // 64t + 32h + (0..31) in byte order.
 __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 qn[8], int& e_out) {
-  // Two passes over the row (the second hits the cache) instead of holding
-  // its 256 bf16 values in 128 registers next to the 64-register result.
+  // One pass over the row: its 256 bf16 values (128 registers, free before
+  // the tile loop) are all loaded before the max is taken.
+  i32x4 raw[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      raw[t][k] = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
   float amax = 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+      const i32x4 v = raw[t][k];
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         amax = fmaxf(amax, fmaxf(fabsf(bf16_lo((unsigned)v[d])), fabsf(bf16_hi((unsigned)v[d]))));
@@ -543,7 +574,7 @@ __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 q
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const i32x4 v = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+      const i32x4 v = raw[t][k];
       const unsigned w0 = (unsigned)v[0], w1 = (unsigned)v[1], w2 = (unsigned)v[2], w3 = (unsigned)v[3];
       qn[t][2 * k] = f32x4_to_fp8x4(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv, bf16_hi(w1) * inv);
       qn[t][2 * k + 1] = f32x4_to_fp8x4(bf16_lo(w2) * inv, bf16_hi(w2) * inv, bf16_lo(w3) * inv, bf16_hi(w3) * inv);
@@ -583,7 +614,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int wave = wave_id();
   const int n = lane & 31, h = lane >> 5;
 
-  int bid = blockIdx.x;
+  int bid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int rg = bid % a.row_groups;
   bid /= a.row_groups;
   const int s = bid % a.splits;
@@ -1056,7 +1087,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int wave = wave_id();
   const int n = lane & 31, h = lane >> 5;
 
-  int bid = blockIdx.x;
+  int bid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int rg = bid % a.row_groups;
   bid /= a.row_groups;
   const int s = bid % a.splits;
