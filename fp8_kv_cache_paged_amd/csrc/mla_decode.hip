@@ -1550,6 +1550,9 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
 // Four workgroups per (group, 32-row block); thread (blk, lane) merges the 16
 // accumulator values that lane held for dv block blk in every split. The
 // partials are normalized by their own row sums; v_scale is applied here.
+// Splits are taken four at a time with all their loads (lse and partial
+// values) issued together, and merged with a running max (every split
+// writes its partial, zeros when empty, so the loads need no guard).
 __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int gr = blockIdx.x >> 2;
   const int g = gr / a.row_blocks;
@@ -1561,29 +1564,45 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims
   if (row >= a.rows) return;
   const long frag0 = (long)g * a.row_blocks + rb;          // split s: frag0 + s * groups * row_blocks
   const long fstride = (long)a.groups * a.row_blocks;
-  float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, part_lse[(frag0 + sp * fstride) * 32 + n]);
+  float M = -INFINITY, W = 0.f;
   float acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  float W = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const long frag = frag0 + sp * fstride;
-      const float ls = part_lse[frag * 32 + n];
-      const float w = ls == -INFINITY ? 0.f : exp2f(ls - M);
-      W += w;
-      const i32x4* src = reinterpret_cast<const i32x4*>(part_o + frag * (16 * 64 * 16) + (blk * 64 + lane) * 16);
-      const i32x4 v0 = src[0], v1 = src[1];
+  for (int s0 = 0; s0 < a.splits; s0 += 4) {
+    float ls[4];
+    i32x4 v0[4], v1[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc[2 * d] += w * half_lo((unsigned)v0[d]);
-        acc[2 * d + 1] += w * half_hi((unsigned)v0[d]);
-        acc[8 + 2 * d] += w * half_lo((unsigned)v1[d]);
-        acc[8 + 2 * d + 1] += w * half_hi((unsigned)v1[d]);
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u < a.splits) {
+        const long frag = frag0 + (s0 + u) * fstride;
+        ls[u] = part_lse[frag * 32 + n];
+        const i32x4* src = reinterpret_cast<const i32x4*>(part_o + frag * (16 * 64 * 16) + (blk * 64 + lane) * 16);
+        v0[u] = src[0];
+        v1[u] = src[1];
+      } else {
+        ls[u] = -INFINITY;
+        v0[u] = v1[u] = i32x4{0, 0, 0, 0};
       }
     }
+    const float m_new = fmaxf(M, fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3])));
+    if (m_new == -INFINITY) continue;
+    const float alpha = exp2f(M - m_new);   // 0 while M = -inf
+    W *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] *= alpha;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = exp2f(ls[u] - m_new);   // 0 for an empty split
+      W += w;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] += w * half_lo((unsigned)v0[u][d]);
+        acc[2 * d + 1] += w * half_hi((unsigned)v0[u][d]);
+        acc[8 + 2 * d] += w * half_lo((unsigned)v1[u][d]);
+        acc[8 + 2 * d + 1] += w * half_hi((unsigned)v1[u][d]);
+      }
+    }
+    M = m_new;
   }
   const float inv = W > 0.f ? *v_scale / W : 0.f;
   const long qrow_idx = (long)g * a.rows + row;
