@@ -547,15 +547,21 @@ struct KDims {
 // n's 512 nope dims. The row's power-of-two exponent needs the amax of both
 // halves (lanes n and n+32). Fragment t (K = 64 dims 64t .. 64t+63) holds dims
 // 64t + 32h + (0..31) in byte order.
-__device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 qn[8], int& e_out) {
-  // One pass over the row: its 256 bf16 values (128 registers, free before
-  // the tile loop) are all loaded before the max is taken.
-  i32x4 raw[8][4];
+// The 256 bf16 query values lane (n, h) quantizes: row n, dims 64 t + 32 h
+// + 8 k .. +7 in raw[t][k]. Unconditional loads (`qrow` must point at a
+// readable row): a per-load guard becomes a branch around each load, after
+// which the compiler waits for the load.
+__device__ inline void load_q_nope_raw(const uint16_t* qrow, int h, i32x4 raw[8][4]) {
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      raw[t][k] = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+      raw[t][k] = *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k);
+}
+
+// Per-row power-of-two scale and e4m3fn codes of the nope query (the row's
+// two lane halves share the max).
+__device__ inline void quantize_q_fp8(const i32x4 raw[8][4], i32x8 qn[8], int& e_out) {
   float amax = 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -581,6 +587,18 @@ __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 q
     }
   }
   e_out = e;
+}
+
+// One pass over the row: its 256 bf16 values (128 registers, free before
+// the tile loop) are all loaded before the max is taken.
+__device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 qn[8], int& e_out) {
+  i32x4 raw[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      raw[t][k] = ok ? *reinterpret_cast<const i32x4*>(qrow + 64 * t + 32 * h + 8 * k) : i32x4{0, 0, 0, 0};
+  quantize_q_fp8(raw, qn, e_out);
 }
 
 // Softmax bookkeeping runs in the log2 domain with a lazily raised running
@@ -1093,6 +1111,27 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int s = bid % a.splits;
   const int g = bid / a.splits;
 
+  const int rb = rg * NW + wave;              // row block of this wave's S^T products
+  const bool wave_active = rb < a.row_blocks;
+  const int row = rb * 32 + n;
+  const bool row_ok = row < a.rows;
+  const long qrow_idx = (long)g * a.rows + row;
+  const uint16_t* qrow = q + qrow_idx * D;
+
+  // The query loads go out first: they depend on nothing else, and their
+  // latency then overlaps the dependent loads (sequence length, page table)
+  // that precede the first tile's copies.
+  // (rows outside the problem read row 0 and are zeroed after quantization)
+  const bool q_ok = row_ok && wave_active;
+  const uint16_t* qsrc = q_ok ? qrow : q;
+  i32x4 qraw[8][4];
+  i32x4 qr_raw[ROPE > 0 ? 4 : 1];
+  load_q_nope_raw(qsrc, h, qraw);
+  if constexpr (ROPE > 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qr_raw[t] = *reinterpret_cast<const i32x4*>(qsrc + kNope + 16 * t + 8 * h);
+  }
+
   const int b = SPARSE ? g / a.s_q : g;
   int sk = seq_lens[b];
   sk = max(0, min(sk, a.max_pages * kKeys));
@@ -1101,19 +1140,12 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int u1 = (int)((long)(s + 1) * units / a.splits);
   const int ntiles = u1 - u0;
 
-  const int rb = rg * NW + wave;              // row block of this wave's S^T products
-  const bool wave_active = rb < a.row_blocks;
-  const int row = rb * 32 + n;
-  const bool row_ok = row < a.rows;
   int row_len = 0;                            // dense: keys this row may see
   if constexpr (!SPARSE) {
     const int i = row / a.h_q;
     row_len = a.causal ? sk - (a.s_q - 1 - i) : sk;
     if (!row_ok) row_len = 0;
   }
-  const long qrow_idx = (long)g * a.rows + row;
-  const uint16_t* qrow = q + qrow_idx * D;
-
   const int32_t* bt_row = block_table + (long)b * a.max_pages;
   const int32_t* idx_row = SPARSE ? indices + (long)g * a.topk : nullptr;
   constexpr long RB = kNope + 2 * ROPE;
@@ -1171,31 +1203,25 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     if (t < 8) xflag[t] = 0;
   }
 
-  // Q fragments (B operand of S^T = K Q^T).
-  i32x8 qn[DOT == DOT_FP8 ? 8 : 1];
-  bf16x8 qb[DOT == DOT_BF16 ? 32 : 1];
+  // Q fragments (B operand of S^T = K Q^T), quantized from the raw values
+  // loaded at entry.
+  i32x8 qn[8];
   bf16x8 qr[ROPE > 0 ? 4 : 1];
   float qk_scale;   // q_scale * k_scale, applied to the nope products
   {
-    const float ks = *k_scale;
-    if constexpr (DOT == DOT_FP8) {
-      int e;
-      stage_q_fp8(qrow, row_ok && wave_active, h, qn, e);
-      qk_scale = ldexpf(ks, e);
-    } else {
-      qk_scale = ks;
+    int e;
+    quantize_q_fp8(qraw, qn, e);
+    qk_scale = ldexpf(*k_scale, e);
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int d0 = 32 * (u >> 1) + 16 * h + 8 * (u & 1);
-        i32x4 v = row_ok ? *reinterpret_cast<const i32x4*>(qrow + d0) : i32x4{0, 0, 0, 0};
-        qb[u] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) qn[t][d] = q_ok ? qn[t][d] : 0;
     if constexpr (ROPE > 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        i32x4 v = row_ok ? *reinterpret_cast<const i32x4*>(qrow + kNope + 16 * t + 8 * h)
-                         : i32x4{0, 0, 0, 0};
+        i32x4 v = qr_raw[t];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] = q_ok ? v[d] : 0;
         qr[t] = __builtin_bit_cast(bf16x8, v);
       }
     }
