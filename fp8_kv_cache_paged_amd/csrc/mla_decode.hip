@@ -348,6 +348,54 @@ __device__ inline void issue_dense_load(uint8_t* lds, int bufi, const uint8_t* p
   }
 }
 
+// The same copies with a scalar base: the uniform part of the source address
+// (page, row) stays in SGPRs, each lane adds a 32-bit offset. The per-lane
+// parts of the offsets are computed once per tile (SpreadLane): for nope load
+// j, lane (hi, p) reads chunk p ^ (2j + hi) of its row, i.e. with x = p ^ hi,
+// chunk x ^ 2j, byte offset hi * RB + ((x << 4) ^ 32 j); for rope load r,
+// lane (r8, p8) reads chunk p8 ^ (4 (r & 1) + r8 / 2), byte offset
+// r8 * RB + 512 + ((y << 4) ^ 64 (r & 1)) with y = p8 ^ (r8 / 2). One
+// xor-add per copy instead of a 64-bit address computation.
+struct SpreadLane {
+  unsigned nx, nrow, rx, rrow;
+};
+template <int ROPE>
+__device__ inline SpreadLane spread_lane() {
+  constexpr int RB = kNope + 2 * ROPE;
+  int lane;   // volatile: recomputed per tile instead of hoisted and spilled
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int hi = lane >> 5, p = lane & 31, r8 = lane >> 3, p8 = lane & 7;
+  return SpreadLane{(unsigned)((p ^ hi) << 4), (unsigned)(hi * RB), (unsigned)((p8 ^ (r8 >> 1)) << 4),
+                    (unsigned)(r8 * RB + kNope)};
+}
+
+__device__ __attribute__((always_inline)) inline void load_lds16_saddr(const uint8_t* sbase, unsigned voff,
+                                                                       uint8_t* lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+  const unsigned long long sb = (unsigned long long)(uintptr_t)sbase;
+  const unsigned long long sbu = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(sb >> 32)) << 32) |
+                                 (unsigned)__builtin_amdgcn_readfirstlane((unsigned)sb);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbu), "s"(m0)
+               : "memory", "m0");
+}
+
+template <int ROPE, int NW>
+__device__ __attribute__((always_inline)) inline void issue_dense_load_s(uint8_t* lds, int bufi, const uint8_t* page_base,
+                                                                         int jj, int wave, const SpreadLane& sl) {
+  constexpr int RB = kNope + 2 * ROPE;
+  constexpr int NJ = 32 / NW, RJ = 8 / NW;
+  if (jj < NJ) {
+    load_lds16_saddr(page_base + (wave * NJ * 2 + 2 * jj) * RB, (sl.nx ^ (32u * (jj & 7))) + sl.nrow,
+                     lds + bufi * kNopeRegion + (wave * NJ + jj) * 1024);
+  } else {
+    const int r = jj - NJ;
+    load_lds16_saddr(page_base + (wave * RJ * 8 + 8 * r) * RB, (sl.rx ^ (64u * (r & 1))) + sl.rrow,
+                     lds + kRopeBase + bufi * kRopeRegion + (wave * RJ + r) * 1024);
+  }
+}
+
 __device__ inline void wait_tile_and_sync() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -1336,6 +1384,8 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     if constexpr (ROPE == 0) Sr[0] = Sr[1] = f32x16{};
     {
       constexpr int NN = 16, NI = NN + (ROPE > 0 ? 8 : 0), PD = 5;
+      const bool spread = __builtin_amdgcn_readfirstlane(spread_page != nullptr ? 1 : 0) != 0;
+      const SpreadLane sl = spread_lane<ROPE>();
       i32x4 rl[PD], rh[PD];
       auto load = [&](int f) {
         const int slot = f % PD, kb = f & 1;
@@ -1358,10 +1408,10 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         if (f + PD == NI) load_pv_operands();
         if constexpr (!SPARSE) {
           constexpr int LPW = Tile<ROPE>::template loads_per_wave<NW>();
-          if (spread_page != nullptr) {
+          if (spread) {
 #pragma unroll
             for (int jj = f * LPW / NI; jj < (f + 1) * LPW / NI; ++jj)
-              issue_dense_load<ROPE, NW>(lds, buf_next, spread_page, jj, wave);
+              issue_dense_load_s<ROPE, NW>(lds, buf_next, spread_page, jj, wave, sl);
           }
         }
         if (f < NN) {
