@@ -1476,15 +1476,15 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     i32x8 pb;
     auto slice = [&](int i) {
       if (i < 4) {
+        // z in place; a tile some row sees only in part (the last of a
+        // sequence) then overwrites its hidden entries with -inf. (Separate
+        // full and masked computations of z end in different registers and
+        // cost a copy per entry where they merge.)
         const int kb = i >> 1, r0 = 8 * (i & 1);
-        if (full) {   // every key of the tile is visible to every row
 #pragma unroll
-          for (int r = r0; r < r0 + 8; ++r) {
-            const float z = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
-            S[kb][r] = z;
-            mx = fmaxf(mx, z);
-          }
-        } else {
+        for (int r = r0; r < r0 + 8; ++r)
+          S[kb][r] = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
+        if (!full) {
 #pragma unroll
           for (int r = r0; r < r0 + 8; ++r) {
             const int j = r >> 2;
@@ -1492,12 +1492,12 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
             bool valid;
             if constexpr (SPARSE) valid = (smask >> key) & 1ull;
             else valid = key < limit;
-            const float zs = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
-            const float z = valid ? zs : -INFINITY;
-            S[kb][r] = z;
-            mx = fmaxf(mx, z);
+            S[kb][r] = valid ? S[kb][r] : -INFINITY;
           }
         }
+#pragma unroll
+        for (int r = r0; r < r0 + 8; ++r) mx = fmaxf(mx, S[kb][r]);
+        asm volatile("" : "+v"(mx));   // keeps each slice's max in its slice
       } else if (i == 4) {
         mx_other = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(mx));
       } else if (i == 6) {
@@ -1518,20 +1518,19 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         }
         m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT>::ps_log2;
       } else if (i >= 7 && i < 15) {
+        // four exponentials, packed to fp8 at once
         const int kb = (i - 7) >> 2, r0 = 4 * ((i - 7) & 3);
+        float pe[4];
 #pragma unroll
-        for (int r = r0; r < r0 + 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(S[kb][r] - m_exp);
-          S[kb][r] = p;
-          psum += p;
+        for (int r = 0; r < 4; ++r) {
+          pe[r] = __builtin_amdgcn_exp2f(S[kb][r0 + r] - m_exp);
+          psum += pe[r];
         }
+        int w = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
+        asm volatile("" : "+v"(w));   // keeps the packing in this slice
+        pb[i - 7] = w;
       } else if (i == 15) {
         l_run += psum;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int kb = q >> 2, r0 = 4 * (q & 3);
-          pb[q] = f32x4_to_fp8x4(S[kb][r0], S[kb][r0 + 1], S[kb][r0 + 2], S[kb][r0 + 3]);
-        }
         uint8_t* pdst = xp + par * X::p_bytes + wave * 2048 + lane * 16;
         *reinterpret_cast<i32x4*>(pdst) = i32x4{pb[0], pb[1], pb[2], pb[3]};
         *reinterpret_cast<i32x4*>(pdst + 1024) = i32x4{pb[4], pb[5], pb[6], pb[7]};
