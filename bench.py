@@ -37,8 +37,10 @@ BF16_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # (a call takes ~0.1 ms: a few hundred warm-up calls are needed for the
+    # GPU's clocks to settle after the bandwidth probe; 10 read ~20% slow)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="metric", choices=sorted(workloads.SPECS))
     ap.add_argument("--dot", default="fp8", choices=["fp8", "bf16"])
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic")
