@@ -6,12 +6,20 @@ usage:
 
 DIR are rocprofv3 output directories (``-d DIR -o NAME --output-format csv``)
 of the same bench.py command: one ``--kernel-trace --stats`` run and two
-``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE). The HBM traffic of the split
-kernel is the per-dispatch counter value scaled by what the same counter reads
-for kernels of known size in the same run: the 2 GiB streaming read that
-bench.py times (FETCH_SIZE) and torch's 2 GiB fill before it (WRITE_SIZE).
-The report records the SHA-256 of the kernel source it was taken with;
-bench.py only reports the traffic while the source is unchanged.
+``--pmc`` runs (FETCH_SIZE, then WRITE_SIZE), plus optionally (``--util DIR``)
+a ``--pmc`` run of the matrix-core and LDS counters (MfmaUtil, LdsUtil,
+LDSBankConflict, LdsBankConflict, SQ_INSTS_VALU_MFMA_MOPS_F8/_BF16).
+
+The HBM traffic of the split kernel is the per-dispatch counter value scaled
+by what the same counter reads for kernels of known size in the same run: the
+2 GiB streaming read that bench.py times (FETCH_SIZE) and torch's 2 GiB fill
+before it (WRITE_SIZE). The report records the SHA-256 of the kernel source it
+was taken with; bench.py only reports the traffic while the source is
+unchanged.
+
+``--per-config NAME=DIR ... --out FILE`` instead summarizes one
+``--kernel-trace --stats`` run per workload: the average duration of the
+split kernel and of the combine kernel of each.
 """
 
 import argparse
@@ -76,15 +84,56 @@ def traffic(fetch_dir, write_dir):
             "write_bytes": write_b, "traffic_bytes": fetch_b + write_b, "dispatches": len(fk)}
 
 
+UTIL_COUNTERS = ["MfmaUtil", "LdsUtil", "LDSBankConflict", "LdsBankConflict",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+
+
+def utilization(util_dir):
+    """Per-dispatch averages of the utilization counters for the split kernel."""
+    out = {}
+    for c in UTIL_COUNTERS:
+        try:
+            v = _match(counter_by_kernel(util_dir, c), SPLIT_KERNEL)
+        except KeyError:
+            continue
+        out[c] = (sum(v) / len(v), len(v))
+    return out
+
+
+def per_config(pairs, out_path, commands):
+    lines = ["# rocprofv3 kernel durations per workload (--kernel-trace --stats)", ""]
+    lines += ["commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):"]
+    lines += [f"  {c}" for c in commands]
+    lines += ["", f"source_sha256: {source_sha256()}", "",
+              f"  {'workload':<14} {'split kernel us':>16} {'calls':>6} {'combine us':>11} {'calls':>6}"]
+    for pair in pairs:
+        name, d = pair.split("=", 1)
+        st = kernel_stats(d)
+        sk = [(c, a) for n, c, a, _ in st if n.startswith("void mla::mla_decode")]
+        ck = [(c, a) for n, c, a, _ in st if "mla_combine_kernel" in n]
+        s_c, s_a = max(sk) if sk else (0, 0.0)
+        c_c, c_a = max(ck) if ck else (0, 0.0)
+        lines.append(f"  {name:<14} {s_a / 1e3:>16.2f} {s_c:>6} {c_a / 1e3:>11.2f} {c_c:>6}")
+    os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--stats", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--util")
+    ap.add_argument("--per-config", nargs="+", default=None, metavar="NAME=DIR")
     ap.add_argument("--bench-json")
     ap.add_argument("--command", action="append", default=[], help="command lines that produced DIRs")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.per_config:
+        per_config(a.per_config, a.out, a.command)
+        return
     st = kernel_stats(a.stats)
     tr = traffic(a.fetch, a.write)
     lines = ["# rocprofv3 summary: mla_decode_kernel (fp8 dots), benchmark workload", ""]
@@ -101,6 +150,13 @@ def main():
               f"  write_bytes_per_launch: {tr['write_bytes']:.0f}",
               f"traffic_bytes_per_launch: {tr['traffic_bytes']:.0f}",
               f"  dispatches averaged: {tr['dispatches']}"]
+    if a.util:
+        ut = utilization(a.util)
+        lines += ["", "matrix-core and LDS counters of the split kernel (--pmc, per dispatch):"]
+        for c, (v, nd) in ut.items():
+            lines.append(f"  {c}: {v:.4g}  ({nd} dispatches)")
+        if "SQ_INSTS_VALU_MFMA_MOPS_F8" in ut:
+            lines.append(f"  fp8 MFMA flops per dispatch (MOPS_F8 x 512): {ut['SQ_INSTS_VALU_MFMA_MOPS_F8'][0] * 512:.4g}")
     if a.bench_json:
         rec = [json.loads(l) for l in open(a.bench_json) if l.strip().startswith("{")][-1]
         rf = rec.get("roofline", {})
