@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of KV copies to rotate through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="decode", choices=["decode", "quantize"],
+                    help="decode (the benchmark) or the quantize-on-write of the benchmark's cache")
     return ap.parse_args()
 
 
@@ -122,6 +124,73 @@ def cpu_baseline(w, budget_s):
                       f"scaled: {sec_per_call:.2f} s per full call"}
 
 
+def main_quantize(args, dev, hbm_meas):
+    """Quantize-on-write of the benchmark shape's whole cache in one call: 64
+    sequences x 8196 tokens of bf16 latent (512) + rope (64) into shuffled
+    64-token pages, the scale computed (amax / 448). Algorithmic bytes per
+    token: 1152 read + 4 (slot) + 640 written."""
+    b, sk = 64, 8196
+    ppseq = (sk + 63) // 64
+    pages = b * ppseq
+    n = b * sk
+    g = torch.Generator(device="cpu").manual_seed(6)
+    ckv = torch.randn((n, 512), generator=g).to(torch.bfloat16).to(dev)
+    rope = torch.randn((n, 64), generator=g).to(torch.bfloat16).to(dev)
+    perm = torch.randperm(pages, generator=g).to(torch.int64)
+    pos = torch.arange(sk)
+    slots = torch.cat([perm[s * ppseq + pos // 64] * 64 + pos % 64 for s in range(b)]).to(torch.int32).to(dev)
+    kv = torch.full((pages, 64, 1, 640), 0xFF, dtype=torch.uint8, device=dev)
+    ks = torch.zeros(1, dtype=torch.float32, device=dev)
+    vs = torch.zeros(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(mla.lib().mla_fp8_quantize_kv_workspace_size(), dtype=torch.uint8, device=dev)
+    mla.quantize_kv(ckv, rope, slots, kv, ks, vs, workspace=ws)
+    import ctypes
+    L = mla.lib()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (n, 64, pages, vp(ckv), vp(rope), vp(slots), vp(kv), vp(ks), vp(vs), 1, vp(ws), ws.numel(), st)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        L.mla_fp8_quantize_kv(*a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        rc = L.mla_fp8_quantize_kv(*a)
+        if rc != 0:
+            raise RuntimeError(mla.status_string(rc))
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = n * (1152 + 4 + 640)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "FP8 KV quantize-on-write GB/s (64 x 8196 tokens, 576-wide latent)",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->fp8", "data": "synthetic",
+        "config": {"workload": f"quantize: {n} tokens, {pages} shuffled pages, scale computed"},
+        "hbm_measured_gbps": round(hbm_meas, 1), "frac_of_measured_hbm": round(gbps / hbm_meas, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "kv_amax_kernel + kv_encode_kernel", "bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import cache
+        m = 16384
+        c_bits = ckv[:m].view(torch.int16).cpu().numpy().view(np.uint16)
+        r_bits = rope[:m].view(torch.int16).cpu().numpy().view(np.uint16)
+        sl = np.arange(m, dtype=np.int32)
+        cache_np = np.full(((m + 63) // 64, 64, 1, 640), 0xFF, dtype=np.uint8)
+        t0 = time.perf_counter()
+        cache.quantize_kv(c_bits, r_bits, sl, cache_np)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(m * (1152 + 4 + 640) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "sample": f"{m} of {n} tokens ({dt:.1f} s)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,6 +205,8 @@ def main():
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.op == "quantize":
+        return main_quantize(args, dev, hbm_read_probe(dev))
 
     w = workloads.make(args.workload)
     flops = workloads.flops(w)

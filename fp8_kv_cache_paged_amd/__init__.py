@@ -100,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.mla_fp8_debug_gather.restype = i32
         L.mla_fp8_bench_stream_read.argtypes = [vp, sz, vp, vp]
         L.mla_fp8_bench_stream_read.restype = i32
+        L.mla_fp8_quantize_kv_workspace_size.argtypes = []
+        L.mla_fp8_quantize_kv_workspace_size.restype = sz
+        L.mla_fp8_quantize_kv.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.mla_fp8_quantize_kv.restype = i32
         _lib = L
     return _lib
 
@@ -242,6 +246,38 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     _check(lib().mla_fp8_bench_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream(stream)),
            "mla_fp8_bench_stream_read")
+
+
+def quantize_kv(ckv: torch.Tensor, k_rope: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+                kv_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor, *,
+                compute_scale: bool = True, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Quantize-on-write of new latent rows into the paged cache (in place).
+
+    ckv bf16 [n, 512], k_rope bf16 [n, 64] or None, slot_mapping int32 [n]
+    (page * 64 + slot; negative or out of range = skipped), kv_cache uint8
+    [pages, 64, 1, 512 + 2 d_rope], k_scale / v_scale f32 [1] on the device.
+    compute_scale: store amax / 448 of the written rows to both scales;
+    otherwise encode with k_scale as given.
+    """
+    n = int(slot_mapping.shape[0])
+    d_rope = 0 if k_rope is None else int(k_rope.shape[1])
+    if ckv.dtype != torch.bfloat16 or ckv.dim() != 2 or ckv.shape[1] != 512 or ckv.shape[0] != n:
+        raise ValueError("ckv must be bf16 [n, 512] with n = len(slot_mapping)")
+    if k_rope is not None and (k_rope.dtype != torch.bfloat16 or k_rope.shape[0] != n):
+        raise ValueError("k_rope must be bf16 [n, d_rope]")
+    if kv_cache.dim() != 4 or kv_cache.shape[1] != 64 or kv_cache.shape[3] != 512 + 2 * d_rope:
+        raise ValueError("kv_cache must be [pages, 64, 1, 512 + 2 * d_rope]")
+    for t in (ckv, k_rope, slot_mapping, kv_cache):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if compute_scale and workspace is None:
+        workspace = torch.empty(lib().mla_fp8_quantize_kv_workspace_size(), dtype=torch.uint8,
+                                device=kv_cache.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_fp8_quantize_kv(n, d_rope, int(kv_cache.shape[0]), _ptr(ckv), _ptr(k_rope),
+                                     _ptr(slot_mapping), _ptr(kv_cache), _ptr(k_scale), _ptr(v_scale),
+                                     1 if compute_scale else 0, _ptr(workspace), ws_bytes, _stream(stream)),
+           "mla_fp8_quantize_kv")
 
 
 def default_softmax_scale(d_nope: int = 512, d_rope: int = 64) -> float:

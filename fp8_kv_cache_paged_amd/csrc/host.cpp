@@ -227,6 +227,41 @@ MLA_API const char* mla_fp8_status_string(int32_t status) {
   }
 }
 
+MLA_API size_t mla_fp8_quantize_kv_workspace_size(void) { return mla::quantize_workspace_bytes(); }
+
+MLA_API int32_t mla_fp8_quantize_kv(int32_t num_tokens, int32_t d_rope, int32_t num_pages, const void* ckv,
+                                    const void* k_rope, const int32_t* slot_mapping, void* kv_cache,
+                                    float* k_scale, float* v_scale, int32_t compute_scale, void* workspace_ptr,
+                                    size_t workspace_bytes, void* hip_stream) {
+  if (num_tokens < 0 || num_pages < 1 || (compute_scale != 0 && compute_scale != 1)) return MLA_ERR_SHAPE;
+  if (d_rope != 0 && d_rope != 64) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)num_pages * kPage > INT32_MAX) return MLA_ERR_SHAPE;
+  if (k_scale == nullptr || v_scale == nullptr || kv_cache == nullptr) return MLA_ERR_NULL;
+  if (num_tokens > 0 && (ckv == nullptr || slot_mapping == nullptr || (d_rope > 0 && k_rope == nullptr)))
+    return MLA_ERR_NULL;
+  if (compute_scale && (workspace_ptr == nullptr || workspace_bytes < mla::quantize_workspace_bytes()))
+    return MLA_ERR_WORKSPACE;
+  if (!aligned(kv_cache, 16) || (ckv != nullptr && !aligned(ckv, 16)) ||
+      (d_rope > 0 && k_rope != nullptr && !aligned(k_rope, 16)) ||
+      (slot_mapping != nullptr && !aligned(slot_mapping, 4)) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+      (workspace_ptr != nullptr && !aligned(workspace_ptr, 4)))
+    return MLA_ERR_ALIGN;
+  if (num_tokens == 0 && !compute_scale) return MLA_OK;
+  mla::QuantizeLaunch d;
+  d.ckv = static_cast<const uint16_t*>(ckv);
+  d.rope = d_rope > 0 ? static_cast<const uint16_t*>(k_rope) : nullptr;
+  d.slots = slot_mapping;
+  d.kv = static_cast<uint8_t*>(kv_cache);
+  d.k_scale = k_scale;
+  d.v_scale = v_scale;
+  d.workspace = compute_scale ? static_cast<float*>(workspace_ptr) : nullptr;
+  d.num_tokens = num_tokens;
+  d.d_rope = d_rope;
+  d.num_pages = num_pages;
+  d.compute_scale = compute_scale != 0;
+  return mla::launch_quantize_kv(d, static_cast<hipStream_t>(hip_stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 MLA_API int32_t mla_fp8_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint16_t* out_bf16, int32_t n,
                                             void* hip_stream) {
   if (codes == nullptr || (out_f32 == nullptr && out_bf16 == nullptr)) return MLA_ERR_NULL;

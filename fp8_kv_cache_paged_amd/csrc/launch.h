@@ -39,6 +39,22 @@ size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks);
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 hipError_t launch_combine(const DecodeLaunch& d, hipStream_t stream);
 
+// A quantize-on-write launch, validated on the host.
+struct QuantizeLaunch {
+  const uint16_t* ckv;     // bf16 [num_tokens, 512]
+  const uint16_t* rope;    // bf16 [num_tokens, d_rope] (d_rope = 64) or null
+  const int32_t* slots;    // [num_tokens] cache row = page * 64 + slot
+  uint8_t* kv;             // [num_pages, 64, 1, 512 + 2 d_rope]
+  float* k_scale;
+  float* v_scale;
+  float* workspace;        // quantize_workspace_bytes(), compute_scale only
+  int32_t num_tokens, d_rope, num_pages;
+  bool compute_scale;
+};
+
+size_t quantize_workspace_bytes();
+hipError_t launch_quantize_kv(const QuantizeLaunch& d, hipStream_t stream);
+
 hipError_t launch_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint16_t* out_bf16,
                                       int32_t n, hipStream_t stream);
 hipError_t launch_debug_quantize_q(const uint16_t* q, int32_t rows, int32_t row_len,

@@ -1,0 +1,176 @@
+// Quantize-on-write of the paged FP8 latent cache for gfx950 (MI355X).
+//
+// The step before the decode (InfiniCore PR #1568, Summary, FP8 KV cache
+// bullet: the per-tensor scale is amax / 448, 448 being the largest finite
+// e4m3fn value): new latent rows (512 bf16 "nope" values and 64 bf16 rope
+// values per token) are written into their cache rows, the nope part as OCP
+// e4m3fn codes of value / scale (round to nearest even, saturating at +-448),
+// the rope part copied unchanged. The cache row is the decode's: 512 code
+// bytes, then the 64 rope values (640 bytes; 512 rope-free). A token's row is
+// slot_mapping[token] = page * 64 + slot; tokens with a negative or
+// out-of-range slot are not written.
+//
+// Two kernels, both HBM-bound streams:
+//  * amax: each workgroup reduces |value| over its share of the written
+//    tokens' nope values and stores one partial (no atomics);
+//  * encode: every workgroup reduces the partials (at most kAmaxGroups
+//    floats), so all of them derive the same scale; workgroup 0 stores it to
+//    k_scale and v_scale. With a given scale the amax kernel is skipped and
+//    the scale is read from k_scale. Each thread then turns 16 input values
+//    into one 16-byte store of the cache row (40 stores per 640-byte row, so
+//    a wave's stores cover whole rows contiguously).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace mla {
+
+namespace {
+
+typedef int q_i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kAmaxGroups = 256;    // partials in the workspace (<= 256 floats)
+constexpr int kQThreads = 256;
+constexpr float kE4m3Max = 448.f;
+
+__device__ inline float bf16_lo_f(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi_f(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ inline bool slot_ok(int slot, long rows) { return slot >= 0 && (long)slot < rows; }
+
+// Max of x over the workgroup (256 threads = 4 waves); valid in thread 0.
+__device__ inline float block_max(float x, float* red) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) x = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return x;
+}
+
+// Partial amax of workgroup blockIdx.x: 16-byte chunks (8 bf16) of the nope
+// values of written tokens, grid-strided.
+__global__ __launch_bounds__(kQThreads) void kv_amax_kernel(const uint16_t* __restrict__ ckv,
+                                                            const int32_t* __restrict__ slots,
+                                                            int num_tokens, long cache_rows,
+                                                            float* __restrict__ partials) {
+  __shared__ float red[4];
+  const long chunks = (long)num_tokens * 64;   // 512 values = 64 chunks per token
+  float m = 0.f;
+  for (long c = (long)blockIdx.x * kQThreads + threadIdx.x; c < chunks; c += (long)gridDim.x * kQThreads) {
+    const long tok = c >> 6;
+    if (!slot_ok(slots[tok], cache_rows)) continue;
+    const q_i32x4 v = *reinterpret_cast<const q_i32x4*>(ckv + c * 8);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      m = fmaxf(m, fmaxf(fabsf(bf16_lo_f((unsigned)v[d])), fabsf(bf16_hi_f((unsigned)v[d]))));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// 4 floats -> 4 e4m3fn bytes, round to nearest even (hardware conversion;
+// the inputs are already within +-448).
+__device__ inline int enc4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
+
+__device__ inline float qv(float x, float scale) {
+  const float y = __fdiv_rn(x, scale);   // correctly rounded f32 division
+  return fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
+}
+
+template <int ROPE>
+__global__ __launch_bounds__(kQThreads) void kv_encode_kernel(const uint16_t* __restrict__ ckv,
+                                                              const uint16_t* __restrict__ rope,
+                                                              const int32_t* __restrict__ slots,
+                                                              int num_tokens, long cache_rows,
+                                                              uint8_t* __restrict__ kv,
+                                                              float* __restrict__ k_scale,
+                                                              float* __restrict__ v_scale,
+                                                              const float* __restrict__ partials,
+                                                              int num_partials) {
+  constexpr int RB = 512 + 2 * ROPE;          // cache row bytes
+  constexpr int CPR = RB / 16;                // 16-byte stores per row
+  __shared__ float red[4];
+  __shared__ float s_scale;
+  if (partials != nullptr) {
+    float m = 0.f;
+    for (int i = threadIdx.x; i < num_partials; i += kQThreads) m = fmaxf(m, partials[i]);
+    m = block_max(m, red);
+    if (threadIdx.x == 0) {
+      const float sc = m > 0.f ? __fdiv_rn(m, kE4m3Max) : 1.f;
+      s_scale = sc;
+      if (blockIdx.x == 0) {
+        *k_scale = sc;
+        *v_scale = sc;
+      }
+    }
+  } else if (threadIdx.x == 0) {
+    s_scale = *k_scale;
+  }
+  __syncthreads();
+  const float scale = s_scale;
+
+  const long chunks = (long)num_tokens * CPR;
+  for (long c = (long)blockIdx.x * kQThreads + threadIdx.x; c < chunks; c += (long)gridDim.x * kQThreads) {
+    const long tok = c / CPR;
+    const int part = (int)(c - tok * CPR);
+    const int slot = slots[tok];
+    if (!slot_ok(slot, cache_rows)) continue;
+    q_i32x4 o;
+    if (part < 32) {
+      // nope values 16 part .. +15 -> 16 code bytes
+      const q_i32x4* src = reinterpret_cast<const q_i32x4*>(ckv + tok * 512 + 16 * part);
+      const q_i32x4 a = src[0], b = src[1];
+      const unsigned w[8] = {(unsigned)a[0], (unsigned)a[1], (unsigned)a[2], (unsigned)a[3],
+                             (unsigned)b[0], (unsigned)b[1], (unsigned)b[2], (unsigned)b[3]};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = enc4(qv(bf16_lo_f(w[2 * k]), scale), qv(bf16_hi_f(w[2 * k]), scale),
+                    qv(bf16_lo_f(w[2 * k + 1]), scale), qv(bf16_hi_f(w[2 * k + 1]), scale));
+    } else {
+      // rope values 8 (part - 32) .. +7, copied
+      o = *reinterpret_cast<const q_i32x4*>(rope + tok * ROPE + 8 * (part - 32));
+    }
+    *reinterpret_cast<q_i32x4*>(kv + (long)slot * RB + 16 * part) = o;
+  }
+}
+
+int grid_for(long work, int cap) {
+  long g = (work + kQThreads - 1) / kQThreads;
+  if (g < 1) g = 1;
+  return (int)(g < cap ? g : cap);
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes() { return kAmaxGroups * sizeof(float); }
+
+hipError_t launch_quantize_kv(const QuantizeLaunch& d, hipStream_t st) {
+  const long rows = (long)d.num_pages * 64;
+  float* partials = nullptr;
+  int np = 0;
+  if (d.compute_scale) {
+    partials = d.workspace;
+    np = grid_for((long)d.num_tokens * 64, kAmaxGroups);
+    hipLaunchKernelGGL(kv_amax_kernel, dim3((unsigned)np), dim3(kQThreads), 0, st, d.ckv, d.slots, d.num_tokens,
+                       rows, partials);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long work = (long)d.num_tokens * ((512 + 2 * d.d_rope) / 16);
+  const int g = grid_for(work, 4096);
+  if (d.d_rope == 64)
+    hipLaunchKernelGGL((kv_encode_kernel<64>), dim3((unsigned)g), dim3(kQThreads), 0, st, d.ckv, d.rope, d.slots,
+                       d.num_tokens, rows, d.kv, d.k_scale, d.v_scale, partials, np);
+  else
+    hipLaunchKernelGGL((kv_encode_kernel<0>), dim3((unsigned)g), dim3(kQThreads), 0, st, d.ckv, d.rope, d.slots,
+                       d.num_tokens, rows, d.kv, d.k_scale, d.v_scale, partials, np);
+  return hipGetLastError();
+}
+
+}  // namespace mla

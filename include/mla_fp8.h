@@ -150,6 +150,38 @@ MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, cons
                                         const int32_t* indices, void* workspace,
                                         size_t workspace_bytes, void* hip_stream);
 
+/* Quantize-on-write of the paged latent cache, the step that fills the cache
+ * the decode reads (InfiniCore PR #1568, Summary, FP8 KV cache bullet: a
+ * per-tensor scale amax / 448, 448 being the largest finite e4m3fn value).
+ *
+ *   ckv           bf16  [num_tokens, 512]     new latent ("nope") rows
+ *   k_rope        bf16  [num_tokens, d_rope]  their rope values (NULL if d_rope = 0)
+ *   slot_mapping  int32 [num_tokens]          cache row of each token: page * 64 +
+ *                                             slot within the page; a negative or
+ *                                             out-of-range entry is skipped (not
+ *                                             written); each row at most once
+ *   kv_cache      bytes [num_pages, 64, 1, 512 + 2 * d_rope], the decode's layout;
+ *                 only the rows named by slot_mapping are written
+ *   k_scale, v_scale  f32[1] device pointers
+ *   compute_scale 1: scale = amax / 448 over the nope values of the written
+ *                 tokens (1 when that amax is 0), computed in f32 and stored to
+ *                 both k_scale and v_scale; needs a workspace of
+ *                 mla_fp8_quantize_kv_workspace_size() bytes.
+ *                 0: the scale is read from k_scale (nothing is stored to the
+ *                 scales; workspace may be NULL).
+ *
+ * A written row holds, for each nope value x, the e4m3fn code of x / scale
+ * (f32, correctly rounded division), clamped to [-448, 448] and rounded to
+ * nearest even; then the d_rope bf16 values copied unchanged. Two kernels
+ * (amax, encode) on hip_stream; no atomics, deterministic. Host checks as for
+ * the decode; a non-finite or non-positive given scale and NaN inputs give
+ * unspecified codes. */
+MLA_API size_t mla_fp8_quantize_kv_workspace_size(void);
+MLA_API int32_t mla_fp8_quantize_kv(int32_t num_tokens, int32_t d_rope, int32_t num_pages, const void* ckv,
+                                    const void* k_rope, const int32_t* slot_mapping, void* kv_cache,
+                                    float* k_scale, float* v_scale, int32_t compute_scale, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream);
+
 /* Static description of a status code. Never NULL. */
 MLA_API const char* mla_fp8_status_string(int32_t status);
 

@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
     assert set(names) <= exported
@@ -155,3 +155,41 @@ def test_debug_exports_check_arguments(L):
                                       None) == mla.MLA_ERR_SHAPE
     assert L.mla_fp8_bench_stream_read(ctypes.c_void_p(16), 17, ctypes.c_void_p(16), None) == mla.MLA_ERR_SHAPE
     assert L.mla_fp8_debug_gather(ctypes.byref(good(h_kv=3)), None, None, None, None, None) == mla.MLA_ERR_UNSUPPORTED
+
+
+# ---- quantize-on-write: host checks (every call returns before a launch) ----
+
+def _q(L, n=4, d_rope=64, pages=2, ckv=16, rope=16, slots=16, kv=16, ks=16, vs=16, cs=1, ws=16,
+       ws_bytes=None):
+    vp = ctypes.c_void_p
+    wsb = L.mla_fp8_quantize_kv_workspace_size() if ws_bytes is None else ws_bytes
+    return L.mla_fp8_quantize_kv(n, d_rope, pages, vp(ckv) if ckv else None, vp(rope) if rope else None,
+                                 vp(slots) if slots else None, vp(kv) if kv else None, vp(ks) if ks else None,
+                                 vp(vs) if vs else None, cs, vp(ws) if ws else None, wsb, None)
+
+
+def test_quantize_workspace_size(L):
+    assert L.mla_fp8_quantize_kv_workspace_size() == 1024
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"n": -1}, mla.MLA_ERR_SHAPE),
+    ({"pages": 0}, mla.MLA_ERR_SHAPE),
+    ({"cs": 2}, mla.MLA_ERR_SHAPE),
+    ({"d_rope": 32}, mla.MLA_ERR_UNSUPPORTED),
+    ({"ks": 0}, mla.MLA_ERR_NULL),
+    ({"vs": 0}, mla.MLA_ERR_NULL),
+    ({"kv": 0}, mla.MLA_ERR_NULL),
+    ({"ckv": 0}, mla.MLA_ERR_NULL),
+    ({"slots": 0}, mla.MLA_ERR_NULL),
+    ({"rope": 0}, mla.MLA_ERR_NULL),
+    ({"ws": 0}, mla.MLA_ERR_WORKSPACE),
+    ({"ws_bytes": 1000}, mla.MLA_ERR_WORKSPACE),
+    ({"ckv": 8}, mla.MLA_ERR_ALIGN),
+    ({"kv": 24}, mla.MLA_ERR_ALIGN),
+    ({"ks": 2}, mla.MLA_ERR_ALIGN),
+    ({"n": 0, "cs": 0}, mla.MLA_OK),                              # nothing to do: no launch
+    ({"n": 0, "cs": 0, "ckv": 0, "slots": 0, "rope": 0}, mla.MLA_OK),
+])
+def test_quantize_host_checks(L, kw, status):
+    assert _q(L, **kw) == status

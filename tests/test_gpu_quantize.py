@@ -1,0 +1,101 @@
+"""GPU parity of the quantize-on-write kernels (through the C ABI) with the
+oracle (oracle/cache.py). Byte path: the cache bytes and the f32 scale must be
+bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_paged_amd as mla
+from oracle import cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def _case(n, d_rope=64, pages=None, seed=0, scale_up=1.0, skip=0):
+    rng = np.random.default_rng(seed)
+    pages = pages or max(1, (n + skip + 63) // 64 + 2)
+    ckv = _bf16_bits(rng.standard_normal((n, 512)) * scale_up)
+    rope = _bf16_bits(rng.standard_normal((n, d_rope))) if d_rope else None
+    slots = rng.permutation(pages * 64)[:n].astype(np.int32)
+    if skip:
+        bad = rng.choice(n, size=skip, replace=False)
+        slots[bad[: skip // 2]] = -1
+        slots[bad[skip // 2:]] = pages * 64 + 5
+    kv = np.full((pages, 64, 1, 512 + 2 * d_rope), 0xFF, dtype=np.uint8)
+    return ckv, rope, slots, kv
+
+
+def _gpu(ckv, rope, slots, kv, scale=None):
+    dev = "cuda:0"
+    c = torch.from_numpy(ckv.view(np.int16)).view(torch.bfloat16).to(dev)
+    r = None if rope is None else torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).to(dev)
+    s = torch.from_numpy(slots).to(dev)
+    k = torch.from_numpy(kv).to(dev)
+    ks = torch.tensor([0.0 if scale is None else float(scale)], dtype=torch.float32, device=dev)
+    vs = torch.tensor([-1.0], dtype=torch.float32, device=dev)
+    mla.quantize_kv(c, r, s, k, ks, vs, compute_scale=scale is None)
+    torch.cuda.synchronize()
+    return k.cpu().numpy(), np.float32(ks.item()), np.float32(vs.item())
+
+
+@pytest.mark.parametrize("n,d_rope,seed,scale_up,skip", [
+    (1, 64, 1, 1.0, 0),
+    (777, 64, 2, 1.0, 0),           # ragged: not a multiple of anything
+    (4096, 64, 3, 3e-3, 0),         # small values: subnormal codes
+    (3000, 0, 4, 20.0, 0),          # rope-free rows
+    (2500, 64, 5, 1.0, 300),        # skipped and out-of-range slots
+])
+def test_quantize_matches_oracle(n, d_rope, seed, scale_up, skip):
+    ckv, rope, slots, kv = _case(n, d_rope, seed=seed, scale_up=scale_up, skip=skip)
+    ref, ref_s = cache.quantize_kv(ckv, rope, slots, kv)
+    got, ks, vs = _gpu(ckv, rope, slots, kv)
+    assert ks.view(np.uint32) == ref_s.view(np.uint32) and vs.view(np.uint32) == ref_s.view(np.uint32)
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_given_scale():
+    ckv, rope, slots, kv = _case(1000, 64, seed=6)
+    ref, _ = cache.quantize_kv(ckv, rope, slots, kv, scale=np.float32(0.0071))
+    got, ks, vs = _gpu(ckv, rope, slots, kv, scale=np.float32(0.0071))
+    assert ks == np.float32(0.0071) and vs == np.float32(-1.0)   # scales not written
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_no_tokens_sets_unit_scale():
+    ckv, rope, slots, kv = _case(0, 64, pages=2, seed=7)
+    got, ks, vs = _gpu(ckv, rope, slots, kv)
+    assert ks == 1.0 and vs == 1.0 and np.array_equal(got, kv)
+
+
+def test_quantize_full_cache_of_the_benchmark_shape():
+    """64 sequences x 8196 tokens in shuffled pages (the decode benchmark's
+    cache, written in one call): scale exact, and rows sampled across the
+    cache bit-exact against the oracle's encoding of the same rows."""
+    b, sk = 64, 8196
+    ppseq = (sk + 63) // 64
+    pages = b * ppseq
+    rng = np.random.default_rng(11)
+    n = b * sk
+    ckv = _bf16_bits(rng.standard_normal((n, 512), dtype=np.float32))
+    rope = _bf16_bits(rng.standard_normal((n, 64), dtype=np.float32))
+    perm = rng.permutation(pages).astype(np.int64)
+    pos = np.arange(sk)
+    slots = np.concatenate([perm[s * ppseq + pos // 64] * 64 + pos % 64 for s in range(b)]).astype(np.int32)
+    kv = np.full((pages, 64, 1, 640), 0xFF, dtype=np.uint8)
+    got, ks, _ = _gpu(ckv, rope, slots, kv)
+    ref_s = cache.kv_scale(ckv, slots, pages * 64)
+    assert ks.view(np.uint32) == ref_s.view(np.uint32)
+    pick = rng.choice(n, size=4096, replace=False)
+    rows = got.reshape(-1, 640)
+    assert np.array_equal(rows[slots[pick], :512], cache.encode_rows(ckv[pick], ref_s))
+    assert np.array_equal(rows[slots[pick], 512:].view("<u2"), rope[pick])
+    # the slack rows of every sequence's last page stay untouched
+    used = np.zeros(pages * 64, dtype=bool)
+    used[slots] = True
+    assert np.all(rows[~used] == 0xFF)
