@@ -31,7 +31,7 @@ namespace {
 
 typedef int q_i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAmaxGroups = 256;    // partials in the workspace (<= 256 floats)
+constexpr int kAmaxGroups = 1024;   // partials in the workspace (<= 1024 floats)
 constexpr int kQThreads = 256;
 constexpr float kE4m3Max = 448.f;
 
@@ -51,21 +51,34 @@ __device__ inline float block_max(float x, float* red) {
 }
 
 // Partial amax of workgroup blockIdx.x: 16-byte chunks (8 bf16) of the nope
-// values of written tokens, grid-strided.
+// values of written tokens, grid-strided, four chunks per thread in flight.
+// The value and slot loads do not depend on each other (a chunk past the end
+// re-reads the last one and is masked), so both go out together.
 __global__ __launch_bounds__(kQThreads) void kv_amax_kernel(const uint16_t* __restrict__ ckv,
                                                             const int32_t* __restrict__ slots,
                                                             int num_tokens, long cache_rows,
                                                             float* __restrict__ partials) {
   __shared__ float red[4];
   const long chunks = (long)num_tokens * 64;   // 512 values = 64 chunks per token
+  const long stride = (long)gridDim.x * kQThreads;
   float m = 0.f;
-  for (long c = (long)blockIdx.x * kQThreads + threadIdx.x; c < chunks; c += (long)gridDim.x * kQThreads) {
-    const long tok = c >> 6;
-    if (!slot_ok(slots[tok], cache_rows)) continue;
-    const q_i32x4 v = *reinterpret_cast<const q_i32x4*>(ckv + c * 8);
+  for (long c0 = (long)blockIdx.x * kQThreads + threadIdx.x; c0 < chunks; c0 += 4 * stride) {
+    q_i32x4 v[4];
+    int sl[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-      m = fmaxf(m, fmaxf(fabsf(bf16_lo_f((unsigned)v[d])), fabsf(bf16_hi_f((unsigned)v[d]))));
+    for (int u = 0; u < 4; ++u) {
+      const long c = c0 + u * stride < chunks ? c0 + u * stride : chunks - 1;
+      v[u] = *reinterpret_cast<const q_i32x4*>(ckv + c * 8);
+      sl[u] = c0 + u * stride < chunks ? slots[c >> 6] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float mu = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        mu = fmaxf(mu, fmaxf(fabsf(bf16_lo_f((unsigned)v[u][d])), fabsf(bf16_hi_f((unsigned)v[u][d]))));
+      m = slot_ok(sl[u], cache_rows) ? fmaxf(m, mu) : m;
+    }
   }
   m = block_max(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
@@ -119,8 +132,9 @@ __global__ __launch_bounds__(kQThreads) void kv_encode_kernel(const uint16_t* __
   for (long c = (long)blockIdx.x * kQThreads + threadIdx.x; c < chunks; c += (long)gridDim.x * kQThreads) {
     const long tok = c / CPR;
     const int part = (int)(c - tok * CPR);
+    // the slot is only needed for the store: the value loads below do not
+    // wait for it
     const int slot = slots[tok];
-    if (!slot_ok(slot, cache_rows)) continue;
     q_i32x4 o;
     if (part < 32) {
       // nope values 16 part .. +15 -> 16 code bytes
@@ -136,7 +150,7 @@ __global__ __launch_bounds__(kQThreads) void kv_encode_kernel(const uint16_t* __
       // rope values 8 (part - 32) .. +7, copied
       o = *reinterpret_cast<const q_i32x4*>(rope + tok * ROPE + 8 * (part - 32));
     }
-    *reinterpret_cast<q_i32x4*>(kv + (long)slot * RB + 16 * part) = o;
+    if (slot_ok(slot, cache_rows)) *reinterpret_cast<q_i32x4*>(kv + (long)slot * RB + 16 * part) = o;
   }
 }
 

@@ -169,7 +169,7 @@ def _q(L, n=4, d_rope=64, pages=2, ckv=16, rope=16, slots=16, kv=16, ks=16, vs=1
 
 
 def test_quantize_workspace_size(L):
-    assert L.mla_fp8_quantize_kv_workspace_size() == 1024
+    assert L.mla_fp8_quantize_kv_workspace_size() == 4096
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -184,7 +184,7 @@ def test_quantize_workspace_size(L):
     ({"slots": 0}, mla.MLA_ERR_NULL),
     ({"rope": 0}, mla.MLA_ERR_NULL),
     ({"ws": 0}, mla.MLA_ERR_WORKSPACE),
-    ({"ws_bytes": 1000}, mla.MLA_ERR_WORKSPACE),
+    ({"ws_bytes": 4000}, mla.MLA_ERR_WORKSPACE),
     ({"ckv": 8}, mla.MLA_ERR_ALIGN),
     ({"kv": 24}, mla.MLA_ERR_ALIGN),
     ({"ks": 2}, mla.MLA_ERR_ALIGN),
