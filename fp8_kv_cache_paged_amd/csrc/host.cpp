@@ -47,7 +47,7 @@ int32_t validate(const mla_params* p) {
     default:
       return MLA_ERR_DTYPE;
   }
-  if (p->batch < 1 || p->s_q < 1 || p->s_q > 16 || p->h_q < 1 || p->h_q > 1024) return MLA_ERR_SHAPE;
+  if (p->batch < 1 || p->s_q < 1 || p->s_q > 1024 || p->h_q < 1 || p->h_q > 1024) return MLA_ERR_SHAPE;
   if (p->num_pages < 1 || p->max_pages_per_seq < 1 || p->topk < 0) return MLA_ERR_SHAPE;
   if (p->causal != 0 && p->causal != 1) return MLA_ERR_SHAPE;
   if (p->dot != MLA_DOT_BF16 && p->dot != MLA_DOT_FP8) return MLA_ERR_SHAPE;

@@ -65,7 +65,8 @@ def good(**kw):
     ({"page_block": 32}, mla.MLA_ERR_UNSUPPORTED),
     ({"batch": 0}, mla.MLA_ERR_SHAPE),
     ({"s_q": 0}, mla.MLA_ERR_SHAPE),
-    ({"s_q": 17}, mla.MLA_ERR_SHAPE),
+    ({"s_q": 1025}, mla.MLA_ERR_SHAPE),
+    ({"s_q": 256}, mla.MLA_OK),
     ({"h_q": 0}, mla.MLA_ERR_SHAPE),
     ({"num_pages": 0}, mla.MLA_ERR_SHAPE),
     ({"max_pages_per_seq": 0}, mla.MLA_ERR_SHAPE),

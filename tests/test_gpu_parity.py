@@ -112,7 +112,8 @@ def test_v_scale_linearity_and_k_scale():
 # ---- the five configurations and the benchmark shape, full size ----------------
 
 FULL = [("tiny", "bf16"), ("tiny", "fp8"), ("mtp", "bf16"), ("mtp", "fp8"), ("varlen", "fp8"),
-        ("large", "bf16"), ("large", "fp8"), ("sparse", "bf16"), ("sparse", "fp8"), ("metric", "fp8")]
+        ("large", "bf16"), ("large", "fp8"), ("sparse", "bf16"), ("sparse", "fp8"), ("metric", "fp8"),
+        ("sparse16", "bf16"), ("sparse16", "fp8"), ("prefill", "bf16"), ("prefill", "fp8")]
 
 
 @pytest.mark.parametrize("name,dot", FULL)

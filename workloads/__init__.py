@@ -60,9 +60,17 @@ SPECS = {
     # the benchmark shape: b=64, s_q=2, sk=8196, h_q=64 (built like "mtp")
     "metric": dict(batch=64, s_q=2, h_q=64, d_rope=64, seq_len=8196, causal=True,
                    num_splits=0, dots=("fp8", "bf16")),
+    # 16-token sparse decode (the aiter PR's second workload, same model shard
+    # as "sparse"): b=2 so that the token count (32) matches "sparse"
+    "sparse16": dict(batch=2, s_q=16, h_q=16, d_rope=0, seq_len=131072, causal=False,
+                     topk=2048, peaky=True, num_splits=0, dots=("bf16", "fp8")),
+    # chunked prefill over the fp8 cache: the last 256 tokens of 4096-token
+    # sequences attend causally to the whole cache (16 heads)
+    "prefill": dict(batch=2, s_q=256, h_q=16, d_rope=64, seq_len=4096, causal=True,
+                    num_splits=0, dots=("bf16", "fp8")),
 }
 
-SEEDS = {"tiny": 1, "mtp": 2, "varlen": 3, "large": 4, "sparse": 5, "metric": 6}
+SEEDS = {"tiny": 1, "mtp": 2, "varlen": 3, "large": 4, "sparse": 5, "metric": 6, "sparse16": 7, "prefill": 8}
 
 
 @dataclass
