@@ -99,3 +99,40 @@ def test_quantize_full_cache_of_the_benchmark_shape():
     used = np.zeros(pages * 64, dtype=bool)
     used[slots] = True
     assert np.all(rows[~used] == 0xFF)
+
+
+def test_quantized_cache_decodes_like_the_oracle():
+    """End to end: the cache written by the quantize kernel, decoded by the
+    decode kernel, against the oracle decode of the oracle-written cache
+    (the two caches are compared byte for byte first)."""
+    from oracle import attn
+    rng = np.random.default_rng(21)
+    b, s_q, h_q, sk = 3, 2, 64, 700
+    ppseq = (sk + 63) // 64
+    pages = b * ppseq + 3
+    perm = rng.permutation(pages)[: b * ppseq].reshape(b, ppseq).astype(np.int32)
+    n = b * sk
+    ckv = _bf16_bits(rng.standard_normal((n, 512)))
+    rope = _bf16_bits(rng.standard_normal((n, 64)))
+    pos = np.arange(sk)
+    slots = np.concatenate([perm[s, pos // 64] * 64 + pos % 64 for s in range(b)]).astype(np.int32)
+    kv0 = np.full((pages, 64, 1, 640), 0xFF, dtype=np.uint8)
+    ref_cache, ref_s = cache.quantize_kv(ckv, rope, slots, kv0)
+    got_cache, ks, vs = _gpu(ckv, rope, slots, kv0)
+    assert ks.view(np.uint32) == ref_s.view(np.uint32) and np.array_equal(got_cache, ref_cache)
+    q_bits = _bf16_bits(rng.standard_normal((b, s_q, h_q, 576)))
+    seq_lens = np.full(b, sk, dtype=np.int32)
+    ref_o, ref_l = attn.mla_decode(q_bits, ref_cache.reshape(pages, 64, 640), perm, seq_lens, float(ref_s),
+                                   float(ref_s), causal=True)
+    dev = "cuda:0"
+    q = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = torch.from_numpy(got_cache).to(dev)
+    bt = torch.from_numpy(perm).to(dev)
+    sl = torch.from_numpy(seq_lens).to(dev)
+    kst = torch.tensor([float(ks)], dtype=torch.float32, device=dev)
+    vst = torch.tensor([float(vs)], dtype=torch.float32, device=dev)
+    out, lse = mla.decode(q, kv, bt, sl, kst, vst, num_splits=0, dot="bf16", causal=True)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    rel = np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o)
+    assert rel <= 5e-3 and np.abs(lse.cpu().numpy() - ref_l).max() <= 1e-3
