@@ -19,7 +19,9 @@ unchanged.
 
 ``--per-config NAME=DIR ... --out FILE`` instead summarizes one
 ``--kernel-trace --stats`` run per workload: the average duration of the
-split kernel and of the combine kernel of each.
+split kernel and of the combine kernel of each; ``--per-config-counters
+NAME=UTIL:FETCH:WRITE ...`` adds the split kernel's utilization counters and
+HBM bytes of the three --pmc runs of a workload.
 """
 
 import argparse
@@ -69,15 +71,15 @@ def _match(d, needle):
     return vals
 
 
-def traffic(fetch_dir, write_dir):
+def traffic(fetch_dir, write_dir, kernel=SPLIT_KERNEL):
     f = counter_by_kernel(fetch_dir, "FETCH_SIZE")
     w = counter_by_kernel(write_dir, "WRITE_SIZE")
     f_probe = _match(f, "stream_read_kernel")
     fetch_scale = STREAM_BYTES / (sum(f_probe) / len(f_probe) * 1024.0)
     w_fill = _match(w, "FillFunctor<unsigned char>")
     write_scale = FILL_BYTES / (sum(w_fill) * 1024.0)   # one fill, split over launches
-    fk = _match(f, SPLIT_KERNEL)
-    wk = _match(w, SPLIT_KERNEL)
+    fk = _match(f, kernel)
+    wk = _match(w, kernel)
     fetch_b = sum(fk) / len(fk) * 1024.0 * fetch_scale
     write_b = sum(wk) / len(wk) * 1024.0 * write_scale
     return {"fetch_scale": fetch_scale, "write_scale": write_scale, "fetch_bytes": fetch_b,
@@ -88,19 +90,35 @@ UTIL_COUNTERS = ["MfmaUtil", "LdsUtil", "LDSBankConflict", "LdsBankConflict",
                  "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
 
 
-def utilization(util_dir):
+def utilization(util_dir, kernel=SPLIT_KERNEL):
     """Per-dispatch averages of the utilization counters for the split kernel."""
     out = {}
     for c in UTIL_COUNTERS:
         try:
-            v = _match(counter_by_kernel(util_dir, c), SPLIT_KERNEL)
+            v = _match(counter_by_kernel(util_dir, c), kernel)
         except KeyError:
             continue
         out[c] = (sum(v) / len(v), len(v))
     return out
 
 
-def per_config(pairs, out_path, commands):
+def per_config_counters(triples):
+    """Lines for --pmc runs per workload: NAME=UTILDIR:FETCHDIR:WRITEDIR."""
+    lines = ["", "split kernel counters per workload (--pmc runs of the same bench.py commands, per dispatch;",
+             "HBM bytes scaled as in the benchmark profile):",
+             f"  {'workload':<10} {'MfmaUtil%':>9} {'LdsUtil%':>8} {'LDSBankConfl%':>13} {'fetch MB':>9} {'write MB':>9}"]
+    any_split = "mla::mla_decode"   # the dv-split or the row-block kernel
+    for t in triples:
+        name, dirs = t.split("=", 1)
+        ud, fd, wd = dirs.split(":")
+        ut = utilization(ud, any_split)
+        tr = traffic(fd, wd, any_split)
+        lines.append(f"  {name:<10} {ut['MfmaUtil'][0]:>9.1f} {ut['LdsUtil'][0]:>8.1f} "
+                     f"{ut['LDSBankConflict'][0]:>13.2f} {tr['fetch_bytes'] / 1e6:>9.1f} {tr['write_bytes'] / 1e6:>9.1f}")
+    return lines
+
+
+def per_config(pairs, out_path, commands, counters=None):
     lines = ["# rocprofv3 kernel durations per workload (--kernel-trace --stats)", ""]
     lines += ["commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):"]
     lines += [f"  {c}" for c in commands]
@@ -114,6 +132,8 @@ def per_config(pairs, out_path, commands):
         s_c, s_a = max(sk) if sk else (0, 0.0)
         c_c, c_a = max(ck) if ck else (0, 0.0)
         lines.append(f"  {name:<14} {s_a / 1e3:>16.2f} {s_c:>6} {c_a / 1e3:>11.2f} {c_c:>6}")
+    if counters:
+        lines += per_config_counters(counters)
     os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -127,12 +147,13 @@ def main():
     ap.add_argument("--write")
     ap.add_argument("--util")
     ap.add_argument("--per-config", nargs="+", default=None, metavar="NAME=DIR")
+    ap.add_argument("--per-config-counters", nargs="+", default=None, metavar="NAME=UTIL:FETCH:WRITE")
     ap.add_argument("--bench-json")
     ap.add_argument("--command", action="append", default=[], help="command lines that produced DIRs")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.per_config:
-        per_config(a.per_config, a.out, a.command)
+        per_config(a.per_config, a.out, a.command, a.per_config_counters)
         return
     st = kernel_stats(a.stats)
     tr = traffic(a.fetch, a.write)
