@@ -10,7 +10,9 @@ What is computed, and where the pages fix it:
   tiles with the rope tile in BF16, and the test report's
   h_kv=1, d=576, dv=512, causal=True parameters).
 * Per-tensor k/v scales on the fp8 part; the cache is quantized with
-  scale = amax/448 (InfiniCore PR #1568, Summary, FP8 KV cache bullet).
+  scale = amax/448 (InfiniCore PR #1568, Summary, FP8 KV cache bullet). The
+  per-token variant the same page names (scales [num_blocks, h_kv,
+  block_size]) takes one k and one v scale per cache row (scale_at).
 * "f32 attention over the same fp8 cache" is the accuracy reference
   (ROCm/aiter PR #6199, Results, Accuracy paragraph): here in float64.
 * Split-KV flash decoding: each split yields a partial (max, sum of exps,
@@ -59,14 +61,30 @@ def _positions_to_rows(kv_cache, block_table_row, pos, page_block):
     return kv_cache[pages, slots]  # [n, row_bytes] uint8
 
 
+def scale_at(scale, block_table_row, pos, page_block=64):
+    """The scale of each key position: a per-tensor scale (a scalar) as is, or
+    per-token scales (an array [pages, page_block], one per cache row) looked
+    up at the positions' rows (InfiniCore PR #1568, Summary: the per-token
+    scale layout [num_blocks, h_kv, block_size])."""
+    s = np.asarray(scale, dtype=np.float64)
+    if s.size == 1:
+        return float(s.reshape(-1)[0])
+    pos = np.asarray(pos, dtype=np.int64)
+    pages = np.asarray(block_table_row)[pos // page_block]
+    return s.reshape(-1, page_block)[pages, pos % page_block]
+
+
 def dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope):
     """Cache rows (uint8 [n, row_bytes]) -> K float64 [n, d_nope+d_rope], V [n, d_nope].
 
     Row layout: d_nope e4m3fn bytes, then d_rope little-endian bf16 values.
+    The scales are scalars or one value per row ([n], see scale_at).
     """
     nope = decode_e4m3fn(rows[:, :d_nope])
-    k = nope * float(k_scale)
-    v = nope * float(v_scale)
+    ks = np.asarray(k_scale, dtype=np.float64)
+    vs = np.asarray(v_scale, dtype=np.float64)
+    k = nope * (ks[:, None] if ks.ndim else float(ks))
+    v = nope * (vs[:, None] if vs.ndim else float(vs))
     if d_rope:
         rb = np.ascontiguousarray(rows[:, d_nope:d_nope + 2 * d_rope])
         rope = bf16_bits_to_f64(rb.view("<u2"))
@@ -132,14 +150,17 @@ def mla_decode(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale, *,
             # every token of the sequence reads a prefix of the same key list
             full = visible_positions(b, s_q - 1, seq_lens, s_q, False)
             rows = _positions_to_rows(kv_cache, block_table[b], full, page_block)
-            k_all, v_all = dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope)
+            k_all, v_all = dequant_keys_values(rows, scale_at(k_scale, block_table[b], full, page_block),
+                                               scale_at(v_scale, block_table[b], full, page_block),
+                                               d_nope, d_rope)
         for i in range(s_q):
             pos = visible_positions(b, i, seq_lens, s_q, causal, indices)
             if indices is None:
                 k, v = k_all[:len(pos)], v_all[:len(pos)]
             else:
                 rows = _positions_to_rows(kv_cache, block_table[b], pos, page_block)
-                k, v = dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope)
+                k, v = dequant_keys_values(rows, scale_at(k_scale, block_table[b], pos, page_block),
+                                           scale_at(v_scale, block_table[b], pos, page_block), d_nope, d_rope)
             out[b, i], lse[b, i] = _attend(q[b, i], k, v, scale)
     return out, lse
 
@@ -175,7 +196,9 @@ def split_partials(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale,
                 for s, (lo, hi) in enumerate(split_ranges(n_units, num_splits)):
                     pos = vis[(vis >= lo * page_block) & (vis < hi * page_block)]
                     rows = _positions_to_rows(kv_cache, block_table[b], pos, page_block)
-                    k, v = dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope)
+                    k, v = dequant_keys_values(rows, scale_at(k_scale, block_table[b], pos, page_block),
+                                               scale_at(v_scale, block_table[b], pos, page_block),
+                                               d_nope, d_rope)
                     o[s, b, i], lse[s, b, i] = _attend(q[b, i], k, v, scale)
             else:
                 entries = np.asarray(indices[b, i]).astype(np.int64)
@@ -184,7 +207,9 @@ def split_partials(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale,
                     part = entries[lo * 64:hi * 64]
                     pos = part[(part >= 0) & (part < sk)]
                     rows = _positions_to_rows(kv_cache, block_table[b], pos, page_block)
-                    k, v = dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope)
+                    k, v = dequant_keys_values(rows, scale_at(k_scale, block_table[b], pos, page_block),
+                                               scale_at(v_scale, block_table[b], pos, page_block),
+                                               d_nope, d_rope)
                     o[s, b, i], lse[s, b, i] = _attend(q[b, i], k, v, scale)
     return o, lse
 

@@ -17,6 +17,10 @@ largest finite e4m3fn value). Readings where the page is silent:
     caller's slot mapping); the row keeps the decode's byte layout: 512 codes,
     then the rope values' little-endian bf16 bytes.
 
+quantize_kv_per_token is the per-token variant (InfiniCore PR #1568,
+Summary: scales laid out [num_blocks, h_kv, block_size]): one scale per
+written row, amax of that row / 448.
+
 Pinned by tests/test_oracle_cache.py: the amax element encodes to +-448
 exactly; every other code is the nearest code of its f32 quotient (brute
 force over all 256 codes); decode(code) * scale reproduces x to half a code
@@ -75,3 +79,26 @@ def quantize_kv(ckv_bits, rope_bits, slot_mapping, kv_cache, scale=None):
         if rope_bits is not None and rope_bits.shape[1] > 0:
             rows[s, 512:] = np.asarray(rope_bits[t], dtype="<u2").view(np.uint8)
     return cache, scale
+
+
+def quantize_kv_per_token(ckv_bits, rope_bits, slot_mapping, kv_cache, scales):
+    """Per-token variant: every written token gets its own f32 scale, the
+    amax of its 512 nope values / 448 (1 if that amax is 0), stored at its
+    cache row in a copy of ``scales`` (f32, one per cache row; the k and v
+    scales of a row are the same value). Returns (new_cache, new_scales)."""
+    cache = np.array(kv_cache, dtype=np.uint8, copy=True)
+    sc = np.array(scales, dtype=np.float32, copy=True).reshape(-1)
+    pages, blk = cache.shape[0], cache.shape[1]
+    rows = cache.reshape(pages * blk, -1)
+    ckv_bits = np.asarray(ckv_bits)
+    for t in range(np.asarray(slot_mapping).shape[0]):
+        s = int(slot_mapping[t])
+        if s < 0 or s >= pages * blk:
+            continue
+        amax = np.float32(np.abs(fp8.bf16_bits_to_f64(ckv_bits[t])).max())
+        st = np.float32(amax / E4M3FN_MAX_F32) if amax > 0 else np.float32(1.0)
+        rows[s, :512] = encode_rows(ckv_bits[t:t + 1], st)[0]
+        if rope_bits is not None and rope_bits.shape[1] > 0:
+            rows[s, 512:] = np.asarray(rope_bits[t], dtype="<u2").view(np.uint8)
+        sc[s] = st
+    return cache, sc.reshape(np.asarray(scales).shape)

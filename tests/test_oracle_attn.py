@@ -129,15 +129,18 @@ def _brute_force(q_bits, cache, bt, seq_lens, ks, vs, d_nope, d_rope, causal, sc
                 zs, vrows = [], []
                 for j in keys:
                     row = cache[bt[bi, j // 64], j % 64]
+                    # per-tensor scales, or per-token arrays [pages, 64]
+                    kss = float(ks[bt[bi, j // 64], j % 64]) if np.ndim(ks) else ks
+                    vss = float(vs[bt[bi, j // 64], j % 64]) if np.ndim(vs) else vs
                     kn = _torch_decode(row[:d_nope])
                     kr = _torch_bf16(row[d_nope:].view(np.uint16)) if d_rope else np.zeros(0)
                     s = 0.0
                     for t in range(d_nope):
-                        s += q[bi, i, h, t] * kn[t] * ks
+                        s += q[bi, i, h, t] * kn[t] * kss
                     for t in range(d_rope):
                         s += q[bi, i, h, d_nope + t] * kr[t]
                     zs.append(scale * s)
-                    vrows.append(kn * vs)
+                    vrows.append(kn * vss)
                 if not zs:
                     continue
                 m = max(zs)
@@ -293,3 +296,63 @@ def test_quantize_q_rows_against_torch_cast():
     np.testing.assert_array_equal(codes, ref)
     amax = np.abs(scaled).max(axis=-1)
     assert np.all(amax[exps != 0] > 224) and np.all(amax <= 448)
+
+
+# ---- per-token scales ([pages, 64], one k and one v scale per cache row) ----
+
+def _per_token_scales(w, seed, spread=8.0):
+    rng = np.random.default_rng(seed)
+    shape = (w.kv_cache.shape[0], 64)
+    ks = (w.k_scale * rng.uniform(1.0 / spread, 1.0, shape)).astype(np.float32)
+    vs = (w.v_scale * rng.uniform(1.0 / spread, 1.0, shape)).astype(np.float32)
+    return ks, vs
+
+
+def test_per_token_scales_brute_force():
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=2, seq_len=[150, 70], seed=41)
+    ks, vs = _per_token_scales(w, 42)
+    out, lse = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, causal=True)
+    ref_o, ref_l = _brute_force(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, 512, 64, True, 1 / 24)
+    np.testing.assert_allclose(out, ref_o, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-11)
+
+
+def test_uniform_per_token_scales_equal_per_tensor():
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=4, seq_len=[300, 5], seed=43)
+    shape = (w.kv_cache.shape[0], 64)
+    ks = np.full(shape, w.k_scale, dtype=np.float64)
+    vs = np.full(shape, w.v_scale, dtype=np.float64)
+    a = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, causal=True)
+    b = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, w.k_scale, w.v_scale, causal=True)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_per_token_v_scales_are_linear_and_unused_rows_do_not_matter():
+    w = workloads.make("tiny", batch=1, s_q=2, h_q=4, seq_len=[130], seed=44)
+    ks, vs = _per_token_scales(w, 45)
+    o1, l1 = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, causal=True)
+    o2, l2 = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, 2 * vs, causal=True)
+    np.testing.assert_allclose(o2, 2 * o1, rtol=1e-13, atol=0)
+    np.testing.assert_array_equal(l1, l2)
+    # scales of rows no sequence uses (slack of the last page, unused pages)
+    used = np.zeros(ks.shape, dtype=bool)
+    pos = np.arange(130)
+    used[w.block_table[0, pos // 64], pos % 64] = True
+    ks3, vs3 = ks.copy(), vs.copy()
+    ks3[~used] = np.nan
+    vs3[~used] = np.nan
+    o3, l3 = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks3, vs3, causal=True)
+    np.testing.assert_array_equal(o3, o1)
+    np.testing.assert_array_equal(l3, l1)
+
+
+@pytest.mark.parametrize("num_splits", [2, 3, 5])
+def test_split_invariance_per_token(num_splits):
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=4, seq_len=[400, 65], seed=46)
+    ks, vs = _per_token_scales(w, 47)
+    o, l = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, causal=True)
+    po, pl = attn.split_partials(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, num_splits, causal=True)
+    co, cl = attn.combine(po, pl)
+    np.testing.assert_allclose(co, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cl, l, rtol=0, atol=1e-12)

@@ -114,3 +114,25 @@ def test_codes_match_torch_float8_cast(scale_up):
     q = np.clip((x / s).astype(np.float32), -448.0, 448.0)
     ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(cache.encode_rows(ckv, s), ref)
+
+
+
+def test_per_token_quantize():
+    """Each written token gets amax / 448 of its own row; its max element is
+    +-448; other rows (cache and scales) are untouched."""
+    ckv, rope, slots, kv = _inputs(24, seed=12)
+    rng = np.random.default_rng(13)
+    x = fp8.bf16_bits_to_f64(ckv) * rng.uniform(0.01, 10.0, (24, 1))
+    ckv = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    scales0 = np.full((kv.shape[0], 64), -1.0, dtype=np.float32)
+    new, sc = cache.quantize_kv_per_token(ckv, rope, slots, kv, scales0)
+    rows = new.reshape(-1, new.shape[-1])
+    vals = fp8.bf16_bits_to_f64(ckv)
+    for t in range(24):
+        st = sc.reshape(-1)[slots[t]]
+        assert st == np.float32(np.float32(np.abs(vals[t]).max()) / np.float32(448.0))
+        d = int(np.argmax(np.abs(vals[t])))
+        assert rows[slots[t], d] == (0xFE if vals[t, d] < 0 else 0x7E)
+        assert np.array_equal(rows[slots[t], :512], cache.encode_rows(ckv[t:t + 1], st)[0])
+    untouched = np.setdiff1d(np.arange(rows.shape[0]), slots)
+    assert np.all(sc.reshape(-1)[untouched] == -1.0) and np.all(rows[untouched] == 0xFF)
