@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of KV copies to rotate through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scales", default="tensor", choices=["tensor", "token"],
+                    help="per-tensor k/v scales, or one per cache row (fp8 dots, dense)")
     ap.add_argument("--op", default="decode", choices=["decode", "quantize"],
                     help="decode (the benchmark) or the quantize-on-write of the benchmark's cache")
     return ap.parse_args()
@@ -222,13 +224,19 @@ def main():
     sl = torch.from_numpy(w.seq_lens).to(dev)
     ks = torch.tensor([w.k_scale], dtype=torch.float32, device=dev)
     vs = torch.tensor([w.v_scale], dtype=torch.float32, device=dev)
+    per_token = args.scales == "token"
+    if per_token:   # one scale per cache row, spread 8x below the per-tensor value
+        g = torch.Generator(device="cpu").manual_seed(7)
+        shape = (w.kv_cache.shape[0], 64)
+        ks = (w.k_scale * (0.125 + 0.875 * torch.rand(shape, generator=g))).to(torch.float32).to(dev)
+        vs = (w.v_scale * (0.125 + 0.875 * torch.rand(shape, generator=g))).to(torch.float32).to(dev)
     idx = None if w.indices is None else torch.from_numpy(w.indices).to(dev)
     kv0 = torch.from_numpy(w.kv_cache).to(dev)
     copies = max(1, int(np.ceil(args.rotate_bytes * (1 << 30) / kv0.numel())))
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
-    p = mla.params_for(q, kv0, bt, causal=w.causal, dot=args.dot, indices=idx)
+    p = mla.params_for(q, kv0, bt, causal=w.causal, dot=args.dot, indices=idx, per_token_scales=per_token)
     splits = args.splits or mla.resolve_splits(p, 0, mla.cu_count(dev))
     ws_bytes = mla.workspace_size(p, splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -237,7 +245,7 @@ def main():
     # points directly with prebuilt arguments, so that host overhead stays far
     # below a kernel's duration and launches queue up back to back
     mla.decode(q, kv0, bt, sl, ks, vs, num_splits=splits, dot=args.dot, causal=w.causal, indices=idx,
-               out=out, lse=lse, workspace=ws)
+               out=out, lse=lse, workspace=ws, per_token_scales=per_token)
     import ctypes
     L = mla.lib()
     vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -302,7 +310,8 @@ def main():
                                f"sk={int(w.seq_lens.max())} d={w.d_nope + w.d_rope} dv={w.d_nope} "
                                f"page=64 {'causal' if w.causal else 'non-causal'}"
                                + (f" topk={w.topk}" if w.topk else ""),
-                   "dots": args.dot, "splits": splits, "kv_copies_rotated": copies},
+                   "dots": args.dot, "splits": splits, "kv_copies_rotated": copies,
+                   "scales": "per token" if per_token else "per tensor"},
         "ms_per_call": round(ms_per_step, 5),
         "hbm_gbps": round(gbps, 1),
         "hbm_measured_gbps": round(hbm_meas, 1),

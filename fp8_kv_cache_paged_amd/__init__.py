@@ -53,7 +53,8 @@ class MlaParams(ctypes.Structure):
     """Mirror of `mla_params` in include/mla_fp8.h."""
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "s_q", "h_q", "h_kv", "d_nope", "d_rope", "dv", "page_block", "num_pages",
-        "max_pages_per_seq", "kv_dtype", "causal", "dot", "topk")] + [("softmax_scale", ctypes.c_float)]
+        "max_pages_per_seq", "kv_dtype", "causal", "dot", "topk")] + [("softmax_scale", ctypes.c_float),
+                                                                          ("kv_scale_per_token", ctypes.c_int32)]
 
 
 class MlaError(RuntimeError):
@@ -130,11 +131,12 @@ def _stream(stream) -> ctypes.c_void_p:
 def make_params(*, batch: int, s_q: int, h_q: int, d_nope: int = 512, d_rope: int = 64,
                 num_pages: int, max_pages_per_seq: int, kv_dtype=torch.uint8, causal: bool = True,
                 dot: str = "fp8", topk: int = 0, softmax_scale: float = 0.0, h_kv: int = 1,
-                page_block: int = 64, dv: Optional[int] = None) -> MlaParams:
+                page_block: int = 64, dv: Optional[int] = None, per_token_scales: bool = False) -> MlaParams:
     code = kv_dtype if isinstance(kv_dtype, int) else _KV_DTYPES.get(kv_dtype, 99)
     return MlaParams(batch, s_q, h_q, h_kv, d_nope, d_rope, d_nope if dv is None else dv, page_block,
                      num_pages, max_pages_per_seq, code, int(bool(causal)),
-                     MLA_DOT_FP8 if dot == "fp8" else MLA_DOT_BF16, topk, float(softmax_scale))
+                     MLA_DOT_FP8 if dot == "fp8" else MLA_DOT_BF16, topk, float(softmax_scale),
+                     int(bool(per_token_scales)))
 
 
 def validate(params: MlaParams) -> int:
@@ -154,7 +156,8 @@ def cu_count(device=None) -> int:
 
 
 def params_for(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, *, causal: bool = True,
-               dot: str = "fp8", indices: Optional[torch.Tensor] = None, softmax_scale: float = 0.0) -> MlaParams:
+               dot: str = "fp8", indices: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+               per_token_scales: bool = False) -> MlaParams:
     """mla_params describing the given tensors (layouts as in include/mla_fp8.h)."""
     b, s_q, h_q, d = q.shape
     row_bytes = kv_cache.shape[-1] * kv_cache.element_size()
@@ -168,7 +171,7 @@ def params_for(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
                        max_pages_per_seq=block_table.shape[1], kv_dtype=kv_cache.dtype, causal=causal,
                        dot=dot, topk=0 if indices is None else indices.shape[-1],
                        softmax_scale=softmax_scale, h_kv=h_kv, page_block=kv_cache.shape[1],
-                       dv=d_nope if d == d_nope + d_rope else -1)
+                       dv=d_nope if d == d_nope + d_rope else -1, per_token_scales=per_token_scales)
 
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
@@ -176,7 +179,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
            causal: bool = True, softmax_scale: float = 0.0, indices: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None,
-           partials_only: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+           partials_only: bool = False, per_token_scales: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode over the paged fp8 cache; returns (out bf16 [b,s_q,h_q,512], lse f32 [b,s_q,h_q]).
 
     q bf16 [b, s_q, h_q, 576|512]; kv_cache uint8/float8_e4m3fn [pages, 64, (1,) 640|512];
@@ -184,7 +187,7 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
     indices int32 [b, s_q, topk] selects the sparse variant.
     """
     p = params_for(q, kv_cache, block_table, causal=causal, dot=dot, indices=indices,
-                   softmax_scale=softmax_scale)
+                   softmax_scale=softmax_scale, per_token_scales=per_token_scales)
     b, s_q, h_q, _ = q.shape
     if out is None:
         out = torch.empty((b, s_q, h_q, 512), dtype=torch.bfloat16, device=q.device)
@@ -250,15 +253,18 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
 
 def quantize_kv(ckv: torch.Tensor, k_rope: Optional[torch.Tensor], slot_mapping: torch.Tensor,
                 kv_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor, *,
-                compute_scale: bool = True, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                compute_scale=True, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Quantize-on-write of new latent rows into the paged cache (in place).
 
     ckv bf16 [n, 512], k_rope bf16 [n, 64] or None, slot_mapping int32 [n]
     (page * 64 + slot; negative or out of range = skipped), kv_cache uint8
     [pages, 64, 1, 512 + 2 d_rope], k_scale / v_scale f32 [1] on the device.
-    compute_scale: store amax / 448 of the written rows to both scales;
-    otherwise encode with k_scale as given.
+    compute_scale: True (or 1) stores amax / 448 of the written rows to both
+    scales; "per_token" (or 2) gives every written row its own scale, stored
+    at its cache row in k_scale / v_scale f32 [pages, 64]; False encodes with
+    k_scale as given.
     """
+    mode = 2 if compute_scale == "per_token" or compute_scale == 2 else (1 if compute_scale else 0)
     n = int(slot_mapping.shape[0])
     d_rope = 0 if k_rope is None else int(k_rope.shape[1])
     if ckv.dtype != torch.bfloat16 or ckv.dim() != 2 or ckv.shape[1] != 512 or ckv.shape[0] != n:
@@ -270,13 +276,13 @@ def quantize_kv(ckv: torch.Tensor, k_rope: Optional[torch.Tensor], slot_mapping:
     for t in (ckv, k_rope, slot_mapping, kv_cache):
         if t is not None and not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-    if compute_scale and workspace is None:
+    if mode == 1 and workspace is None:
         workspace = torch.empty(lib().mla_fp8_quantize_kv_workspace_size(), dtype=torch.uint8,
                                 device=kv_cache.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mla_fp8_quantize_kv(n, d_rope, int(kv_cache.shape[0]), _ptr(ckv), _ptr(k_rope),
                                      _ptr(slot_mapping), _ptr(kv_cache), _ptr(k_scale), _ptr(v_scale),
-                                     1 if compute_scale else 0, _ptr(workspace), ws_bytes, _stream(stream)),
+                                     mode, _ptr(workspace), ws_bytes, _stream(stream)),
            "mla_fp8_quantize_kv")
 
 

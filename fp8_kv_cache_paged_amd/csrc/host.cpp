@@ -50,6 +50,7 @@ int32_t validate(const mla_params* p) {
   if (p->batch < 1 || p->s_q < 1 || p->s_q > 1024 || p->h_q < 1 || p->h_q > 1024) return MLA_ERR_SHAPE;
   if (p->num_pages < 1 || p->max_pages_per_seq < 1 || p->topk < 0) return MLA_ERR_SHAPE;
   if (p->causal != 0 && p->causal != 1) return MLA_ERR_SHAPE;
+  if (p->kv_scale_per_token != 0 && p->kv_scale_per_token != 1) return MLA_ERR_SHAPE;
   if (p->dot != MLA_DOT_BF16 && p->dot != MLA_DOT_FP8) return MLA_ERR_SHAPE;
   if (!(p->softmax_scale <= 0.f || isfinite(p->softmax_scale))) return MLA_ERR_SHAPE;
   if (p->h_kv != 1 || p->d_nope != 512 || p->dv != p->d_nope || p->page_block != kPage ||
@@ -58,6 +59,8 @@ int32_t validate(const mla_params* p) {
   // index arithmetic in the kernels is 32-bit on rows and 64-bit on bytes
   if ((int64_t)p->num_pages * kPage > INT32_MAX) return MLA_ERR_SHAPE;
   if ((int64_t)p->max_pages_per_seq * kPage > INT32_MAX) return MLA_ERR_SHAPE;
+  // per-token scales: the dense fp8-dot kernel only
+  if (p->kv_scale_per_token && (p->dot != MLA_DOT_FP8 || p->topk > 0)) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)p->batch * p->s_q * p->h_q > INT32_MAX / 1024) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
@@ -164,6 +167,7 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   d.gather_v = gv != nullptr && gv[0] == '1';
   const char* rk = getenv("MLA_FP8_ROWS_KERNEL");
   d.rows_kernel = rk != nullptr && rk[0] == '1';
+  d.per_token = p->kv_scale_per_token != 0;
   const char* dbg = getenv("MLA_FP8_DEBUG");
   d.debug_print = dbg != nullptr && dbg[0] == '1';
   if (d.debug_print)
@@ -233,20 +237,20 @@ MLA_API int32_t mla_fp8_quantize_kv(int32_t num_tokens, int32_t d_rope, int32_t 
                                     const void* k_rope, const int32_t* slot_mapping, void* kv_cache,
                                     float* k_scale, float* v_scale, int32_t compute_scale, void* workspace_ptr,
                                     size_t workspace_bytes, void* hip_stream) {
-  if (num_tokens < 0 || num_pages < 1 || (compute_scale != 0 && compute_scale != 1)) return MLA_ERR_SHAPE;
+  if (num_tokens < 0 || num_pages < 1 || compute_scale < 0 || compute_scale > 2) return MLA_ERR_SHAPE;
   if (d_rope != 0 && d_rope != 64) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)num_pages * kPage > INT32_MAX) return MLA_ERR_SHAPE;
   if (k_scale == nullptr || v_scale == nullptr || kv_cache == nullptr) return MLA_ERR_NULL;
   if (num_tokens > 0 && (ckv == nullptr || slot_mapping == nullptr || (d_rope > 0 && k_rope == nullptr)))
     return MLA_ERR_NULL;
-  if (compute_scale && (workspace_ptr == nullptr || workspace_bytes < mla::quantize_workspace_bytes()))
+  if (compute_scale == 1 && (workspace_ptr == nullptr || workspace_bytes < mla::quantize_workspace_bytes()))
     return MLA_ERR_WORKSPACE;
   if (!aligned(kv_cache, 16) || (ckv != nullptr && !aligned(ckv, 16)) ||
       (d_rope > 0 && k_rope != nullptr && !aligned(k_rope, 16)) ||
       (slot_mapping != nullptr && !aligned(slot_mapping, 4)) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
       (workspace_ptr != nullptr && !aligned(workspace_ptr, 4)))
     return MLA_ERR_ALIGN;
-  if (num_tokens == 0 && !compute_scale) return MLA_OK;
+  if (num_tokens == 0 && compute_scale != 1) return MLA_OK;   // nothing to write
   mla::QuantizeLaunch d;
   d.ckv = static_cast<const uint16_t*>(ckv);
   d.rope = d_rope > 0 ? static_cast<const uint16_t*>(k_rope) : nullptr;
@@ -254,11 +258,12 @@ MLA_API int32_t mla_fp8_quantize_kv(int32_t num_tokens, int32_t d_rope, int32_t 
   d.kv = static_cast<uint8_t*>(kv_cache);
   d.k_scale = k_scale;
   d.v_scale = v_scale;
-  d.workspace = compute_scale ? static_cast<float*>(workspace_ptr) : nullptr;
+  d.workspace = compute_scale == 1 ? static_cast<float*>(workspace_ptr) : nullptr;
   d.num_tokens = num_tokens;
   d.d_rope = d_rope;
   d.num_pages = num_pages;
   d.compute_scale = compute_scale != 0;
+  d.per_token = compute_scale == 2;
   return mla::launch_quantize_kv(d, static_cast<hipStream_t>(hip_stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -30,6 +30,7 @@ struct DecodeLaunch {
   float softmax_scale;
   bool gather_v;       // debug: byte-gather V^T fragments instead of transposed LDS reads
   bool rows_kernel;    // fp8 dots: P.V split by row block (as for bf16 dots) instead of by dv
+  bool per_token;      // k_scale, v_scale: one per cache row ([num_pages, 64])
   bool debug_print;
 };
 
@@ -50,6 +51,7 @@ struct QuantizeLaunch {
   float* workspace;        // quantize_workspace_bytes(), compute_scale only
   int32_t num_tokens, d_rope, num_pages;
   bool compute_scale;
+  bool per_token;          // compute_scale: one scale per written row
 };
 
 size_t quantize_workspace_bytes();

@@ -53,6 +53,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -166,6 +167,15 @@ __device__ __attribute__((always_inline)) inline void load_lds16(const uint8_t* 
   // cannot prove that.
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+// The same with 4 bytes per lane (lane l's dword lands at lds_base + 4 l).
+__device__ __attribute__((always_inline)) inline void load_lds4(const void* src, uint8_t* lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(src), "s"(m0)
                : "memory", "m0");
@@ -582,6 +592,7 @@ struct KDims {
   int32_t s_q, h_q, rows, row_blocks, row_groups, groups, splits;
   int32_t num_pages, max_pages, topk, causal;
   float sm_log2;  // softmax_scale * log2(e)
+  int32_t per_token;  // k_scale, v_scale hold one value per cache row
 };
 
 #define MLA_KERNEL_PTRS                                                                   \
@@ -1134,17 +1145,25 @@ struct Xchg {
 // transposing V reads are the costliest LDS traffic of a tile). The S^T
 // products and the softmax stay with the wave that owns the row block; P^T
 // and the rescale factors cross through LDS, one tile behind.
-template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V>
+// PT (per-token scales): k_scale and v_scale hold one value per cache row
+// ([num_pages, 64]). Each tile copy then also moves the page's 64 k- and 64
+// v-scales into LDS; the softmax multiplies each nope sum by its key's
+// k-scale, and each p by its key's v-scale over V_ref, the split's largest
+// v-scale (so P stays within e4m3fn's range); O is scaled by V_ref at the end.
+template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V, bool PT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   static_assert(DOT == DOT_FP8, "the dv-split kernel is for fp8 dots");
+  static_assert(!(PT && SPARSE), "per-token scales: dense only");
   constexpr int D = kNope + ROPE;               // q row length
   constexpr int kJ = 16 / NW;                   // 32-wide dv blocks per wave in P.V
   using X = Xchg<NW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + X::bytes];
+  constexpr int kScaleBytes = PT ? kBufs * 512 : 0;   // per ring buffer: 64 k-, 64 v-scales
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + X::bytes + kScaleBytes];
   uint8_t* const lds = lds_;
   uint8_t* const xp = lds + Tile<ROPE>::lds_bytes;
+  uint8_t* const xs = xp + X::bytes;            // PT: scales of ring buffer i at xs + 512 i
   float* const xalpha = reinterpret_cast<float*>(xp + 2 * X::p_bytes);
   int* const xflag = reinterpret_cast<int*>(xp + X::flag_off);
   float* const xfin = reinterpret_cast<float*>(xp + X::fin_off);
@@ -1218,9 +1237,21 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   auto page_of_lane = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
   int pages_v = -1;
   auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
+  // PT: the page's 64 k-scales (wave 0) and 64 v-scales (wave 1, or 0) go
+  // to the scale slot of ring buffer bufi. A missing page moves none: its
+  // keys are masked, and every use of a scale is guarded by that mask.
+  auto issue_scales = [&](int page, int bufi) {
+    if constexpr (PT) {
+      if (page_valid(page)) {
+        if (wave == 0) load_lds4(k_scale + (long)page * kKeys + lane, xs + bufi * 512);
+        if (wave == (NW > 1 ? 1 : 0)) load_lds4(v_scale + (long)page * kKeys + lane, xs + bufi * 512 + 256);
+      }
+    }
+  };
   auto issue_dense = [&](int unit, int page, int bufi) {
     const bool ok = page_valid(page);
     const int valid = ok ? min(kKeys, sk - unit * kKeys) : 0;
+    issue_scales(page, bufi);
     issue_dense_tile<ROPE, NW>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, lane, wave);
   };
 
@@ -1259,7 +1290,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   {
     int e;
     quantize_q_fp8(qraw, qn, e);
-    qk_scale = ldexpf(*k_scale, e);
+    qk_scale = ldexpf(PT ? 1.f : *k_scale, e);   // PT: k-scales apply per key
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -1282,6 +1313,29 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   if constexpr (!SPARSE) pages_v = page_of_lane(u0 + lane);
   wait_vmcnt<0>();
   asm volatile("" : "+v"(pages_v));   // loaded before the loop, not inside it
+
+  // PT: V_ref = the largest v-scale of the split's valid rows (1 if none).
+  float vref = 1.f, inv_vref = 1.f;
+  if constexpr (PT) {
+    float vm = 0.f;
+    for (int c = 0; c < ntiles; c += 64) {
+      const int pg = c + lane < ntiles ? bt_row[u0 + c + lane] : -1;
+      for (int t = 0; t < 64 && c + t < ntiles; ++t) {
+        const int page = __builtin_amdgcn_readlane(pg, t);
+        if (page_valid(page)) {
+          const int valid = min(kKeys, sk - (u0 + c + t) * kKeys);
+          if (lane < valid) vm = fmaxf(vm, v_scale[(long)page * kKeys + lane]);
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) vm = fmaxf(vm, __shfl_xor(vm, o));
+    vm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, vm)));
+    if (vm > 0.f) {
+      vref = vm;
+      inv_vref = 1.f / vm;
+    }
+    wait_vmcnt<0>();
+  }
 
   const LdsBases lb(lane);
   // V^T lane bases of this wave's dv blocks (block wave * kJ + j, j < kJ)
@@ -1327,6 +1381,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         const bool ok = page_valid(page_next);
         if (ok && sk - t1u(t1) * kKeys >= kKeys) {
           spread_page = kv + (long)page_next * kKeys * RB;
+          issue_scales(page_next, buf_next);
         } else {
           issue_dense(u0 + t1, page_next, buf_next);
         }
@@ -1481,9 +1536,24 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         // full and masked computations of z end in different registers and
         // cost a copy per entry where they merge.)
         const int kb = i >> 1, r0 = 8 * (i & 1);
+        if constexpr (PT) {
+          // k-scales of this slice's keys: 32 kb + 8 j + 4 ((j + h) & 1) + (r & 3), j = r / 4
+          const uint8_t* xk = xs + buf * 512;
 #pragma unroll
-        for (int r = r0; r < r0 + 8; ++r)
-          S[kb][r] = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = (r0 >> 2) + jj;
+            const f32x4 ks = *reinterpret_cast<const f32x4*>(xk + 4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)));
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int r = 4 * j + rr;
+              S[kb][r] = ROPE > 0 ? fmaf(Sn[kb][r] * ks[rr], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * ks[rr] * cn;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = r0; r < r0 + 8; ++r)
+            S[kb][r] = ROPE > 0 ? fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2) : Sn[kb][r] * cn;
+        }
         if (!full) {
 #pragma unroll
           for (int r = r0; r < r0 + 8; ++r) {
@@ -1526,6 +1596,15 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
           pe[r] = __builtin_amdgcn_exp2f(S[kb][r0 + r] - m_exp);
           psum += pe[r];
         }
+        if constexpr (PT) {
+          // p times its key's v-scale / V_ref (<= 1); masked keys (p = 0)
+          // skip the scale, which may be stale or garbage
+          const int j = r0 >> 2;
+          const f32x4 vs = *reinterpret_cast<const f32x4*>(xs + buf * 512 + 256 +
+                                                           4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pe[r] = pe[r] > 0.f ? pe[r] * (vs[r] * inv_vref) : 0.f;
+        }
         int w = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
         asm volatile("" : "+v"(w));   // keeps the packing in this slice
         pb[i - 7] = w;
@@ -1565,7 +1644,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   const bool nonempty = l_tot > 0.f;
   // splits == 1: output scale v_scale / l; else the partials' 1 / l (fp16
   // partials, |value| <= 448; the combine applies v_scale)
-  if (h == 0) xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? *v_scale : 1.f) / l_tot : 0.f;
+  if (h == 0) xfin[wave * 32 + n] = nonempty ? (PT ? vref : (a.splits == 1 ? *v_scale : 1.f)) / l_tot : 0.f;
   if (wave_active && h == 0) {
     const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
     if (a.splits == 1) {
@@ -1679,7 +1758,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims
     }
     M = m_new;
   }
-  const float inv = W > 0.f ? *v_scale / W : 0.f;
+  const float inv = W > 0.f ? (a.per_token ? 1.f : *v_scale) / W : 0.f;   // per token: in the partials
   const long qrow_idx = (long)g * a.rows + row;
   uint16_t* orow = out + qrow_idx * kNope;
 #pragma unroll
@@ -1782,6 +1861,7 @@ static KDims make_dims(const DecodeLaunch& d) {
   a.groups = d.groups; a.splits = d.splits;
   a.num_pages = d.num_pages; a.max_pages = d.max_pages; a.topk = d.topk; a.causal = d.causal;
   a.sm_log2 = d.softmax_scale * kLog2e;
+  a.per_token = d.per_token ? 1 : 0;
   return a;
 }
 
@@ -1812,6 +1892,20 @@ static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t s
 // bf16 dots the row-block kernel.
 template <int DOT, int ROPE, bool SPARSE>
 static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  if constexpr (DOT == DOT_FP8 && !SPARSE) {
+    if (d.per_token) {
+      const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
+      switch (waves_per_group(d.row_blocks)) {
+        case 1: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, false, 1, false, true>), grid, dim3(64), 0, st,
+                                   MLA_PTR_ARGS(d), a); break;
+        case 2: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, false, 2, false, true>), grid, dim3(128), 0, st,
+                                   MLA_PTR_ARGS(d), a); break;
+        default: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, false, 4, false, true>), grid, dim3(256), 0, st,
+                                    MLA_PTR_ARGS(d), a); break;
+      }
+      return hipGetLastError();
+    }
+  }
   if constexpr (DOT == DOT_FP8) {
     if (d.rows_kernel) return launch_nw<DOT, ROPE, SPARSE, false, false>(d, a, st);
     return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, true>(d, a, st)

@@ -154,6 +154,45 @@ __global__ __launch_bounds__(kQThreads) void kv_encode_kernel(const uint16_t* __
   }
 }
 
+// Per-token scales: one wave per token. Lane l holds nope values 8l .. 8l+7;
+// the row's amax is a wave reduction, its scale amax / 448 (1 if 0) is stored
+// at the row's slot in k_scale and v_scale, and lanes 0-7 copy the rope.
+template <int ROPE>
+__global__ __launch_bounds__(kQThreads) void kv_encode_per_token_kernel(const uint16_t* __restrict__ ckv,
+                                                                        const uint16_t* __restrict__ rope,
+                                                                        const int32_t* __restrict__ slots,
+                                                                        int num_tokens, long cache_rows,
+                                                                        uint8_t* __restrict__ kv,
+                                                                        float* __restrict__ k_scale,
+                                                                        float* __restrict__ v_scale) {
+  constexpr int RB = 512 + 2 * ROPE;
+  const int lane = threadIdx.x & 63;
+  const long tok = (long)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
+  if (tok >= num_tokens) return;
+  const int slot = slots[tok];
+  if (!slot_ok(slot, cache_rows)) return;   // wave-uniform
+  const q_i32x4 v = *reinterpret_cast<const q_i32x4*>(ckv + tok * 512 + 8 * lane);
+  float m = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) m = fmaxf(m, fmaxf(fabsf(bf16_lo_f((unsigned)v[d])), fabsf(bf16_hi_f((unsigned)v[d]))));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const float scale = m > 0.f ? __fdiv_rn(m, kE4m3Max) : 1.f;
+  const int c0 = enc4(qv(bf16_lo_f((unsigned)v[0]), scale), qv(bf16_hi_f((unsigned)v[0]), scale),
+                      qv(bf16_lo_f((unsigned)v[1]), scale), qv(bf16_hi_f((unsigned)v[1]), scale));
+  const int c1 = enc4(qv(bf16_lo_f((unsigned)v[2]), scale), qv(bf16_hi_f((unsigned)v[2]), scale),
+                      qv(bf16_lo_f((unsigned)v[3]), scale), qv(bf16_hi_f((unsigned)v[3]), scale));
+  uint8_t* row = kv + (long)slot * RB;
+  *reinterpret_cast<uint2*>(row + 8 * lane) = uint2{(unsigned)c0, (unsigned)c1};
+  if constexpr (ROPE > 0) {
+    if (lane < 8) *reinterpret_cast<q_i32x4*>(row + 512 + 16 * lane) =
+        *reinterpret_cast<const q_i32x4*>(rope + tok * ROPE + 8 * lane);
+  }
+  if (lane == 0) {
+    k_scale[slot] = scale;
+    v_scale[slot] = scale;
+  }
+}
+
 int grid_for(long work, int cap) {
   long g = (work + kQThreads - 1) / kQThreads;
   if (g < 1) g = 1;
@@ -166,6 +205,16 @@ size_t quantize_workspace_bytes() { return kAmaxGroups * sizeof(float); }
 
 hipError_t launch_quantize_kv(const QuantizeLaunch& d, hipStream_t st) {
   const long rows = (long)d.num_pages * 64;
+  if (d.per_token) {
+    const dim3 grid((unsigned)((d.num_tokens + kQThreads / 64 - 1) / (kQThreads / 64)));
+    if (d.d_rope == 64)
+      hipLaunchKernelGGL((kv_encode_per_token_kernel<64>), grid, dim3(kQThreads), 0, st, d.ckv, d.rope, d.slots,
+                         d.num_tokens, rows, d.kv, d.k_scale, d.v_scale);
+    else
+      hipLaunchKernelGGL((kv_encode_per_token_kernel<0>), grid, dim3(kQThreads), 0, st, d.ckv, d.rope, d.slots,
+                         d.num_tokens, rows, d.kv, d.k_scale, d.v_scale);
+    return hipGetLastError();
+  }
   float* partials = nullptr;
   int np = 0;
   if (d.compute_scale) {

@@ -113,6 +113,12 @@ typedef struct mla_params {
   int32_t dot;                /* MLA_DOT_BF16 or MLA_DOT_FP8 */
   int32_t topk;               /* 0 = dense paged; > 0 = sparse, indices required */
   float softmax_scale;        /* <= 0 selects 1/sqrt(d_nope + d_rope) */
+  int32_t kv_scale_per_token; /* 0: k_scale, v_scale are f32[1] (per tensor);
+                                 1: f32 [num_pages, 1, 64], one k and one v scale
+                                 per cache row (InfiniCore PR #1568, Summary: the
+                                 [num_blocks, h_kv, block_size] layout). Dense
+                                 decode with MLA_DOT_FP8 only, else
+                                 MLA_ERR_UNSUPPORTED */
 } mla_params;
 
 /* Host-only validation of *p (no HIP call). Returns MLA_OK or the first
@@ -165,6 +171,10 @@ MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, cons
  *   kv_cache      bytes [num_pages, 64, 1, 512 + 2 * d_rope], the decode's layout;
  *                 only the rows named by slot_mapping are written
  *   k_scale, v_scale  f32[1] device pointers
+ *   compute_scale 2: per token: each written row gets its own scale, amax of
+ *                 its 512 nope values / 448 (1 if 0), stored at its cache row in
+ *                 k_scale and v_scale, here f32 [num_pages, 1, 64] arrays (the
+ *                 layout of kv_scale_per_token); no workspace.
  *   compute_scale 1: scale = amax / 448 over the nope values of the written
  *                 tokens (1 when that amax is 0), computed in f32 and stored to
  *                 both k_scale and v_scale; needs a workspace of

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(mla.MlaParams) == 15 * 4
+    assert ctypes.sizeof(mla.MlaParams) == 16 * 4
 
 
 def good(**kw):
@@ -66,6 +66,9 @@ def good(**kw):
     ({"batch": 0}, mla.MLA_ERR_SHAPE),
     ({"s_q": 0}, mla.MLA_ERR_SHAPE),
     ({"s_q": 1025}, mla.MLA_ERR_SHAPE),
+    ({"per_token_scales": True}, mla.MLA_OK),
+    ({"per_token_scales": True, "dot": "bf16"}, mla.MLA_ERR_UNSUPPORTED),
+    ({"per_token_scales": True, "topk": 64}, mla.MLA_ERR_UNSUPPORTED),
     ({"s_q": 256}, mla.MLA_OK),
     ({"h_q": 0}, mla.MLA_ERR_SHAPE),
     ({"num_pages": 0}, mla.MLA_ERR_SHAPE),
@@ -176,7 +179,8 @@ def test_quantize_workspace_size(L):
 @pytest.mark.parametrize("kw,status", [
     ({"n": -1}, mla.MLA_ERR_SHAPE),
     ({"pages": 0}, mla.MLA_ERR_SHAPE),
-    ({"cs": 2}, mla.MLA_ERR_SHAPE),
+    ({"cs": 3}, mla.MLA_ERR_SHAPE),
+    ({"n": 0, "cs": 2, "ws": 0}, mla.MLA_OK),                     # per token, nothing to write
     ({"d_rope": 32}, mla.MLA_ERR_UNSUPPORTED),
     ({"ks": 0}, mla.MLA_ERR_NULL),
     ({"vs": 0}, mla.MLA_ERR_NULL),

@@ -1,0 +1,109 @@
+"""GPU parity of per-token KV scales (one k and one v scale per cache row,
+[pages, 64]) through the C ABI: the per-token quantize-on-write bit for bit,
+and the fp8-dot decode within the fp8-dot tolerances against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_paged_amd as mla
+import gpu_util as gu
+import workloads
+from oracle import attn, cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def _scales(w, seed, spread=8.0):
+    rng = np.random.default_rng(seed)
+    shape = (w.kv_cache.shape[0], 64)
+    ks = (w.k_scale * rng.uniform(1.0 / spread, 1.0, shape)).astype(np.float32)
+    vs = (w.v_scale * rng.uniform(1.0 / spread, 1.0, shape)).astype(np.float32)
+    return ks, vs
+
+
+def _decode(w, ks, vs, splits):
+    t = gu.device_inputs(w)
+    kst = torch.from_numpy(ks).to("cuda:0")
+    vst = torch.from_numpy(vs).to("cuda:0")
+    out, lse = mla.decode(t["q"], t["kv"], t["bt"], t["sl"], kst, vst, num_splits=splits, dot="fp8",
+                          causal=w.causal, per_token_scales=True)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(w, ks, vs, splits):
+    out, lse = _decode(w, ks, vs, splits)
+    kw = dict(d_nope=w.d_nope, d_rope=w.d_rope, causal=w.causal, softmax_scale=w.softmax_scale)
+    ref_o, ref_l = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, **kw)
+    qp = attn.dequantized_q_nope(w.q_bits)
+    _, ref_lq = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, q_nope_override=qp, **kw)
+    return gu.compare(out, lse, ref_o, ref_l, ref_lq, "fp8")
+
+
+CASES = [
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 64, "seq_len": [700, 3], "seed": 121}),      # 4 waves, ragged
+    ("tiny", {"batch": 3, "s_q": 2, "h_q": 48, "seq_len": [130, 64, 2], "seed": 122}),  # 96 rows
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 32, "seq_len": [257, 90], "seed": 123}),     # 2 waves
+    ("tiny", {"batch": 2, "s_q": 1, "h_q": 16, "seq_len": [200, 33], "seed": 124}),     # 1 wave
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 64, "d_rope": 0, "seq_len": [300, 64], "seed": 125}),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES)
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_per_token_decode_matches_oracle(name, kw, splits):
+    w = workloads.make(name, **kw)
+    ks, vs = _scales(w, kw["seed"])
+    res = _check(w, ks, vs, splits)
+    print(f"per-token {kw} splits={splits}: {res}")
+
+
+def test_per_token_decode_benchmark_shape():
+    w = workloads.make("metric")
+    ks, vs = _scales(w, 126)
+    res = _check(w, ks, vs, 0)
+    print(f"per-token metric: {res}")
+
+
+def test_per_token_quantize_then_decode():
+    rng = np.random.default_rng(127)
+    b, s_q, h_q, sk = 3, 2, 64, 600
+    ppseq = (sk + 63) // 64
+    pages = b * ppseq + 2
+    perm = rng.permutation(pages)[: b * ppseq].reshape(b, ppseq).astype(np.int32)
+    n = b * sk
+    # row magnitudes spread 4x, so the per-token scales differ (a wider spread
+    # makes the logits of the largest rows dominate, and the fp8 query's own
+    # rounding, not the scales, then sets the error)
+    x = rng.standard_normal((n, 512)) * rng.uniform(0.5, 2.0, (n, 1))
+    ckv = _bf16_bits(x)
+    rope = _bf16_bits(rng.standard_normal((n, 64)))
+    pos = np.arange(sk)
+    slots = np.concatenate([perm[s, pos // 64] * 64 + pos % 64 for s in range(b)]).astype(np.int32)
+    kv0 = np.full((pages, 64, 1, 640), 0xFF, dtype=np.uint8)
+    sc0 = np.zeros((pages, 64), dtype=np.float32)
+    ref_cache, ref_sc = cache.quantize_kv_per_token(ckv, rope, slots, kv0, sc0)
+    dev = "cuda:0"
+    kv = torch.from_numpy(kv0).to(dev)
+    ks = torch.from_numpy(sc0).to(dev)
+    vs = torch.from_numpy(sc0).to(dev)
+    mla.quantize_kv(torch.from_numpy(ckv.view(np.int16)).view(torch.bfloat16).to(dev),
+                    torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).to(dev),
+                    torch.from_numpy(slots).to(dev), kv, ks, vs, compute_scale="per_token")
+    torch.cuda.synchronize()
+    assert np.array_equal(kv.cpu().numpy(), ref_cache)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), ref_sc.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), ref_sc.view(np.uint32))
+    q_bits = _bf16_bits(rng.standard_normal((b, s_q, h_q, 576)))
+    w = workloads.Workload(**{**workloads.make("tiny").__dict__, "batch": b, "s_q": s_q, "h_q": h_q,
+                              "q_bits": q_bits, "kv_cache": ref_cache.reshape(pages, 64, 640),
+                              "block_table": perm, "seq_lens": np.full(b, sk, dtype=np.int32),
+                              "indices": None, "causal": True})
+    res = _check(w, ref_sc, ref_sc, 0)
+    print(f"per-token quantize -> decode: {res}")
