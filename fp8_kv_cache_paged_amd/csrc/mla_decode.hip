@@ -172,12 +172,22 @@ __device__ __attribute__((always_inline)) inline void load_lds16(const uint8_t* 
                : "memory", "m0");
 }
 
-// The same with 4 bytes per lane (lane l's dword lands at lds_base + 4 l).
-__device__ __attribute__((always_inline)) inline void load_lds4(const void* src, uint8_t* lds_base) {
+// 64 consecutive dwords from a wave-uniform source to lds_base (lane l's
+// dword lands at lds_base + 4 l). The source stays in SGPRs and the lane
+// offset comes from the exec-mask bit count at the call (a per-lane 64-bit
+// address kept across the tile loop would be spilled, and its reload would
+// wait for every copy in flight).
+__device__ __attribute__((always_inline)) inline void load_lds4_row(const float* sbase, uint8_t* lds_base) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+  const unsigned long long sb = (unsigned long long)(uintptr_t)sbase;
+  const unsigned long long sbu = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(sb >> 32)) << 32) |
+                                 (unsigned)__builtin_amdgcn_readfirstlane((unsigned)sb);
+  unsigned voff;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 2, %0"
+               : "=v"(voff));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :
-               : "v"(src), "s"(m0)
+               : "v"(voff), "s"(sbu), "s"(m0)
                : "memory", "m0");
 }
 
@@ -1243,8 +1253,8 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   auto issue_scales = [&](int page, int bufi) {
     if constexpr (PT) {
       if (page_valid(page)) {
-        if (wave == 0) load_lds4(k_scale + (long)page * kKeys + lane, xs + bufi * 512);
-        if (wave == (NW > 1 ? 1 : 0)) load_lds4(v_scale + (long)page * kKeys + lane, xs + bufi * 512 + 256);
+        if (wave == 0) load_lds4_row(k_scale + (long)page * kKeys, xs + bufi * 512);
+        if (wave == (NW > 1 ? 1 : 0)) load_lds4_row(v_scale + (long)page * kKeys, xs + bufi * 512 + 256);
       }
     }
   };
@@ -1529,6 +1539,22 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     bool flagged = false;
     float psum = 0.f, m_exp = 0.f;
     i32x8 pb;
+    // PT: the scales a slice needs are read one slice ahead (a read used at
+    // once would stall the slice for the LDS latency): k-scales of slice i
+    // (< 4) for keys 32 kb + 8 j + 4 ((j + h) & 1) + 0..3, j = 2 (i & 1) + 0..1;
+    // v-scales of slice i (7..14) for j = (i - 7) & 3, kb = (i - 7) >> 2.
+    f32x4 ks_next[2], vs_next;
+    auto scale_key4 = [&](int kb, int j) { return 4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)); };
+    auto fetch_k = [&](int i) {
+      if constexpr (PT) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          ks_next[jj] = *reinterpret_cast<const f32x4*>(xs + buf * 512 + scale_key4(i >> 1, 2 * (i & 1) + jj));
+      }
+    };
+    auto fetch_v = [&](int i) {
+      if constexpr (PT) vs_next = *reinterpret_cast<const f32x4*>(xs + buf * 512 + 256 + scale_key4((i - 7) >> 2, (i - 7) & 3));
+    };
     auto slice = [&](int i) {
       if (i < 4) {
         // z in place; a tile some row sees only in part (the last of a
@@ -1537,12 +1563,12 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         // cost a copy per entry where they merge.)
         const int kb = i >> 1, r0 = 8 * (i & 1);
         if constexpr (PT) {
-          // k-scales of this slice's keys: 32 kb + 8 j + 4 ((j + h) & 1) + (r & 3), j = r / 4
-          const uint8_t* xk = xs + buf * 512;
+          const f32x4 ksc[2] = {ks_next[0], ks_next[1]};   // this slice's k-scales
+          if (i + 1 < 4) fetch_k(i + 1);
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = (r0 >> 2) + jj;
-            const f32x4 ks = *reinterpret_cast<const f32x4*>(xk + 4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)));
+            const f32x4 ks = ksc[jj];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int r = 4 * j + rr;
@@ -1571,6 +1597,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       } else if (i == 4) {
         mx_other = __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(mx));
       } else if (i == 6) {
+        fetch_v(7);
         mx = fmaxf(mx, __int_as_float(mx_other));
         const bool raise = mx > m_run + Soft<DOT>::tau;
         if (__ballot(raise)) {
@@ -1599,9 +1626,8 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
         if constexpr (PT) {
           // p times its key's v-scale / V_ref (<= 1); masked keys (p = 0)
           // skip the scale, which may be stale or garbage
-          const int j = r0 >> 2;
-          const f32x4 vs = *reinterpret_cast<const f32x4*>(xs + buf * 512 + 256 +
-                                                           4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)));
+          const f32x4 vs = vs_next;
+          if (i + 1 < 15) fetch_v(i + 1);
 #pragma unroll
           for (int r = 0; r < 4; ++r) pe[r] = pe[r] > 0.f ? pe[r] * (vs[r] * inv_vref) : 0.f;
         }
@@ -1619,6 +1645,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
 
     // O^T += V^T P^T for tile k-1: dv block j of this wave's kJ times row
     // block r, 16 MFMAs, with a softmax slice after each.
+    fetch_k(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = i / NW, r = i % NW;
