@@ -191,6 +191,15 @@ __device__ __attribute__((always_inline)) inline void load_lds4_row(const float*
                : "memory", "m0");
 }
 
+// One dword per lane from per-lane sources (lane l's lands at lds_base + 4 l).
+__device__ __attribute__((always_inline)) inline void load_lds4_gather(const float* src, uint8_t* lds_base) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
 // Max of a value over lanes l and l ^ 32 (the two halves holding one query row).
 __device__ inline float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
@@ -1165,7 +1174,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   static_assert(DOT == DOT_FP8, "the dv-split kernel is for fp8 dots");
-  static_assert(!(PT && SPARSE), "per-token scales: dense only");
   constexpr int D = kNope + ROPE;               // q row length
   constexpr int kJ = 16 / NW;                   // 32-wide dv blocks per wave in P.V
   using X = Xchg<NW>;
@@ -1258,6 +1266,15 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
       }
     }
   };
+  // PT, sparse: tile row l's scales (row = cache row of entry l, -1 when
+  // skipped: then row 0, whose key is masked) to the slot of ring buffer bufi.
+  auto issue_sparse_scales = [&](int row, int bufi) {
+    if constexpr (PT && SPARSE) {
+      const long r = row >= 0 ? row : 0;
+      if (wave == 0) load_lds4_gather(k_scale + r, xs + bufi * 512);
+      if (wave == (NW > 1 ? 1 : 0)) load_lds4_gather(v_scale + r, xs + bufi * 512 + 256);
+    }
+  };
   auto issue_dense = [&](int unit, int page, int bufi) {
     const bool ok = page_valid(page);
     const int valid = ok ? min(kKeys, sk - unit * kKeys) : 0;
@@ -1271,6 +1288,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   if (ntiles > 0) {
     if constexpr (SPARSE) {
       row_cur = sparse_row(u0 * kKeys + lane);
+      issue_sparse_scales(row_cur, 0);
       issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
     } else {
       page_cur = page_of(u0);
@@ -1328,13 +1346,21 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   float vref = 1.f, inv_vref = 1.f;
   if constexpr (PT) {
     float vm = 0.f;
-    for (int c = 0; c < ntiles; c += 64) {
-      const int pg = c + lane < ntiles ? bt_row[u0 + c + lane] : -1;
-      for (int t = 0; t < 64 && c + t < ntiles; ++t) {
-        const int page = __builtin_amdgcn_readlane(pg, t);
-        if (page_valid(page)) {
-          const int valid = min(kKeys, sk - (u0 + c + t) * kKeys);
-          if (lane < valid) vm = fmaxf(vm, v_scale[(long)page * kKeys + lane]);
+    if constexpr (SPARSE) {
+      // the rows the split's index entries name (lane l: entry 64 t + l)
+      for (int t = 0; t < ntiles; ++t) {
+        const int row = sparse_row((u0 + t) * kKeys + lane);
+        if (row >= 0) vm = fmaxf(vm, v_scale[row]);
+      }
+    } else {
+      for (int c = 0; c < ntiles; c += 64) {
+        const int pg = c + lane < ntiles ? bt_row[u0 + c + lane] : -1;
+        for (int t = 0; t < 64 && c + t < ntiles; ++t) {
+          const int page = __builtin_amdgcn_readlane(pg, t);
+          if (page_valid(page)) {
+            const int valid = min(kKeys, sk - (u0 + c + t) * kKeys);
+            if (lane < valid) vm = fmaxf(vm, v_scale[(long)page * kKeys + lane]);
+          }
         }
       }
     }
@@ -1376,6 +1402,7 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     if (k + 1 < ntiles) {
       if constexpr (SPARSE) {
         row_next = sparse_row((u0 + k + 1) * kKeys + lane);
+        issue_sparse_scales(row_next, buf_next);
         issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
       } else {
         const int t1 = k + 1;
@@ -1919,15 +1946,15 @@ static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t s
 // bf16 dots the row-block kernel.
 template <int DOT, int ROPE, bool SPARSE>
 static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
-  if constexpr (DOT == DOT_FP8 && !SPARSE) {
+  if constexpr (DOT == DOT_FP8) {
     if (d.per_token) {
       const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
       switch (waves_per_group(d.row_blocks)) {
-        case 1: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, false, 1, false, true>), grid, dim3(64), 0, st,
+        case 1: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 1, false, true>), grid, dim3(64), 0, st,
                                    MLA_PTR_ARGS(d), a); break;
-        case 2: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, false, 2, false, true>), grid, dim3(128), 0, st,
+        case 2: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 2, false, true>), grid, dim3(128), 0, st,
                                    MLA_PTR_ARGS(d), a); break;
-        default: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, false, 4, false, true>), grid, dim3(256), 0, st,
+        default: hipLaunchKernelGGL((mla_decode_kernel<DOT, ROPE, SPARSE, 4, false, true>), grid, dim3(256), 0, st,
                                     MLA_PTR_ARGS(d), a); break;
       }
       return hipGetLastError();
