@@ -59,8 +59,6 @@ int32_t validate(const mla_params* p) {
   // index arithmetic in the kernels is 32-bit on rows and 64-bit on bytes
   if ((int64_t)p->num_pages * kPage > INT32_MAX) return MLA_ERR_SHAPE;
   if ((int64_t)p->max_pages_per_seq * kPage > INT32_MAX) return MLA_ERR_SHAPE;
-  // per-token scales: the fp8-dot kernels only
-  if (p->kv_scale_per_token && p->dot != MLA_DOT_FP8) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)p->batch * p->s_q * p->h_q > INT32_MAX / 1024) return MLA_ERR_SHAPE;
   return MLA_OK;
 }

@@ -698,13 +698,19 @@ template <> struct Soft<0> { static constexpr float tau = 8.f, ps_log2 = 0.f; };
 // Decode with the P.V products split over the waves by row block: each wave
 // owns 32 query rows end to end (S^T, softmax, P.V over all 512 dv). Used for
 // bf16 dots, whose P^T operands are too large to exchange between waves.
-template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V>
+// PT (per-token scales, as in the dv-split kernel): each tile copy also moves
+// the 64 rows' k- and v-scales into LDS; the nope sums are multiplied by their
+// key's k-scale, and p by its key's v-scale before the bf16 packing (bf16 has
+// the range, so no reference scale is needed).
+template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V, bool PT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1)))
 void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
+  static_assert(!(PT && DOT == DOT_FP8), "per-token scales with fp8 dots use the dv-split kernel");
   constexpr int D = kNope + ROPE;               // q row length
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + (PT ? kBufs * 512 : 0)];
   uint8_t* const lds = lds_;
+  uint8_t* const xs = lds + Tile<ROPE>::lds_bytes;   // PT: scales of ring buffer i at xs + 512 i
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -764,7 +770,20 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   auto issue_dense = [&](int unit, int page, int bufi) {
     const bool ok = page_valid(page);
     const int valid = ok ? min(kKeys, sk - unit * kKeys) : 0;
+    if constexpr (PT) {
+      if (ok) {
+        if (wave == 0) load_lds4_row(k_scale + (long)page * kKeys, xs + bufi * 512);
+        if (wave == (NW > 1 ? 1 : 0)) load_lds4_row(v_scale + (long)page * kKeys, xs + bufi * 512 + 256);
+      }
+    }
     issue_dense_tile<ROPE, NW>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, lane, wave);
+  };
+  auto issue_sparse_scales = [&](int row, int bufi) {
+    if constexpr (PT && SPARSE) {
+      const long r = row >= 0 ? row : 0;   // a skipped entry's key is masked
+      if (wave == 0) load_lds4_gather(k_scale + r, xs + bufi * 512);
+      if (wave == (NW > 1 ? 1 : 0)) load_lds4_gather(v_scale + r, xs + bufi * 512 + 256);
+    }
   };
 
   // Dense tiles are loaded two ahead (tiles k+1 and k+2 land while tile k
@@ -774,6 +793,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   if (ntiles > 0) {
     if constexpr (SPARSE) {
       row_cur = sparse_row(u0 * kKeys + lane);
+      issue_sparse_scales(row_cur, 0);
       issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
     } else {
       page_cur = page_of(u0);
@@ -789,7 +809,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   bf16x8 qr[ROPE > 0 ? 4 : 1];
   float qk_scale;   // q_scale * k_scale, applied to the nope accumulator
   {
-    const float ks = *k_scale;
+    const float ks = PT ? 1.f : *k_scale;   // PT: k-scales apply per key
     if constexpr (DOT == DOT_FP8) {
       int e;
       stage_q_fp8(qrow, row_ok && wave_active, h, qn, e);
@@ -845,6 +865,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
     if constexpr (SPARSE) {
       if (k + 1 < ntiles) {
         row_next = sparse_row((u0 + k + 1) * kKeys + lane);
+        issue_sparse_scales(row_next, buf_next);
         issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
       }
     } else {
@@ -948,8 +969,20 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         __builtin_amdgcn_sched_barrier(0);
         if (ROPE > 0 && f == NN - 1) {
           s_nop_result2(Sn[0], Sn[1]);
-          Sn[0] *= qk_scale;
-          Sn[1] *= qk_scale;
+          if constexpr (PT) {
+            // key of register r of block kb: 32 kb + 8 j + 4 ((j + h) & 1) + (r & 3), j = r / 4
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const f32x4 ksv = *reinterpret_cast<const f32x4*>(xs + buf * 512 + 4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)));
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Sn[kb][4 * j + rr] *= qk_scale * ksv[rr];
+              }
+          } else {
+            Sn[0] *= qk_scale;
+            Sn[1] *= qk_scale;
+          }
         }
       }
     }
@@ -985,7 +1018,10 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         float zs;
         if constexpr (kSepRope) zs = fmaf(Sn[kb][r], cn, Sr[kb][r] * a.sm_log2);
         else if constexpr (ROPE > 0) zs = Sn[kb][r] * a.sm_log2;   // bf16: scaled already
-        else zs = Sn[kb][r] * cn;
+        else if constexpr (PT) {
+          const int j = r >> 2;
+          zs = Sn[kb][r] * cn * reinterpret_cast<const float*>(xs + buf * 512)[32 * kb + 8 * j + 4 * ((j + h) & 1) + (r & 3)];
+        } else zs = Sn[kb][r] * cn;
         const float z = (full || valid) ? zs : -INFINITY;
         S[kb][r] = z;
         mx = fmaxf(mx, z);
@@ -1061,6 +1097,20 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      if constexpr (PT) {
+        // p times its key's v-scale; masked keys (p = 0) skip the scale
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 vsv = *reinterpret_cast<const f32x4*>(xs + buf * 512 + 256 + 4 * (32 * kb + 8 * j + 4 * ((j + h) & 1)));
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const float p = S[kb][4 * j + rr];
+              S[kb][4 * j + rr] = p > 0.f ? p * vsv[rr] : 0.f;
+            }
+          }
+      }
       bf16x8 pb[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1103,7 +1153,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   const bool nonempty = l_tot > 0.f;
   // splits == 1: the output, scaled by v_scale; else the partials, normalized
   // by the row sum only (fp16, |value| <= 448; the combine applies v_scale)
-  const float inv = nonempty ? (a.splits == 1 ? *v_scale : 1.f) / l_tot : 0.f;
+  const float inv = nonempty ? (PT ? 1.f : (a.splits == 1 ? *v_scale : 1.f)) / l_tot : 0.f;
   const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
 
   if (a.splits == 1) {
@@ -1965,6 +2015,18 @@ static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t s
     return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, true>(d, a, st)
                       : launch_nw<DOT, ROPE, SPARSE, false, true>(d, a, st);
   } else {
+    if (d.per_token) {
+      const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
+      switch (waves_per_group(d.row_blocks)) {
+        case 1: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 1, false, true>), grid, dim3(64), 0,
+                                   st, MLA_PTR_ARGS(d), a); break;
+        case 2: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 2, false, true>), grid, dim3(128), 0,
+                                   st, MLA_PTR_ARGS(d), a); break;
+        default: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 4, false, true>), grid, dim3(256), 0,
+                                    st, MLA_PTR_ARGS(d), a); break;
+      }
+      return hipGetLastError();
+    }
     return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, false>(d, a, st)
                       : launch_nw<DOT, ROPE, SPARSE, false, false>(d, a, st);
   }

@@ -116,9 +116,7 @@ typedef struct mla_params {
   int32_t kv_scale_per_token; /* 0: k_scale, v_scale are f32[1] (per tensor);
                                  1: f32 [num_pages, 1, 64], one k and one v scale
                                  per cache row (InfiniCore PR #1568, Summary: the
-                                 [num_blocks, h_kv, block_size] layout).
-                                 MLA_DOT_FP8 only (dense or sparse), else
-                                 MLA_ERR_UNSUPPORTED */
+                                 [num_blocks, h_kv, block_size] layout) */
 } mla_params;
 
 /* Host-only validation of *p (no HIP call). Returns MLA_OK or the first

@@ -67,7 +67,7 @@ def good(**kw):
     ({"s_q": 0}, mla.MLA_ERR_SHAPE),
     ({"s_q": 1025}, mla.MLA_ERR_SHAPE),
     ({"per_token_scales": True}, mla.MLA_OK),
-    ({"per_token_scales": True, "dot": "bf16"}, mla.MLA_ERR_UNSUPPORTED),
+    ({"per_token_scales": True, "dot": "bf16"}, mla.MLA_OK),
     ({"per_token_scales": True, "topk": 64}, mla.MLA_OK),
     ({"s_q": 256}, mla.MLA_OK),
     ({"h_q": 0}, mla.MLA_ERR_SHAPE),

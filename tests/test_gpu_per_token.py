@@ -1,6 +1,7 @@
 """GPU parity of per-token KV scales (one k and one v scale per cache row,
 [pages, 64]) through the C ABI: the per-token quantize-on-write bit for bit,
-and the fp8-dot decode within the fp8-dot tolerances against the oracle."""
+and the decode (fp8 and bf16 dots, dense and sparse) within the dot mode's
+tolerances against the oracle."""
 
 import numpy as np
 import pytest
@@ -27,25 +28,25 @@ def _scales(w, seed, spread=8.0):
     return ks, vs
 
 
-def _decode(w, ks, vs, splits):
+def _decode(w, ks, vs, splits, dot="fp8"):
     t = gu.device_inputs(w)
     kst = torch.from_numpy(ks).to("cuda:0")
     vst = torch.from_numpy(vs).to("cuda:0")
-    out, lse = mla.decode(t["q"], t["kv"], t["bt"], t["sl"], kst, vst, num_splits=splits, dot="fp8",
+    out, lse = mla.decode(t["q"], t["kv"], t["bt"], t["sl"], kst, vst, num_splits=splits, dot=dot,
                           causal=w.causal, indices=t["idx"], softmax_scale=w.softmax_scale or 0.0,
                           per_token_scales=True)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _check(w, ks, vs, splits):
-    out, lse = _decode(w, ks, vs, splits)
+def _check(w, ks, vs, splits, dot="fp8"):
+    out, lse = _decode(w, ks, vs, splits, dot)
     kw = dict(d_nope=w.d_nope, d_rope=w.d_rope, causal=w.causal, softmax_scale=w.softmax_scale,
               indices=w.indices)
     ref_o, ref_l = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, **kw)
     qp = attn.dequantized_q_nope(w.q_bits)
     _, ref_lq = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, q_nope_override=qp, **kw)
-    return gu.compare(out, lse, ref_o, ref_l, ref_lq, "fp8")
+    return gu.compare(out, lse, ref_o, ref_l, ref_lq if dot == "fp8" else ref_l, dot)
 
 
 CASES = [
@@ -67,25 +68,28 @@ SPREAD = {"tiny": 8.0, "sparse": 2.0}
 
 @pytest.mark.parametrize("name,kw", CASES)
 @pytest.mark.parametrize("splits", [1, 3, 0])
-def test_per_token_decode_matches_oracle(name, kw, splits):
+@pytest.mark.parametrize("dot", ["fp8", "bf16"])
+def test_per_token_decode_matches_oracle(name, kw, splits, dot):
     w = workloads.make(name, **kw)
     ks, vs = _scales(w, kw["seed"], SPREAD[name])
-    res = _check(w, ks, vs, splits)
-    print(f"per-token {kw} splits={splits}: {res}")
+    res = _check(w, ks, vs, splits, dot)
+    print(f"per-token {dot} {kw} splits={splits}: {res}")
 
 
-def test_per_token_decode_sparse_configuration():
+@pytest.mark.parametrize("dot", ["fp8", "bf16"])
+def test_per_token_decode_sparse_configuration(dot):
     w = workloads.make("sparse")
     ks, vs = _scales(w, 129, SPREAD["sparse"])
-    res = _check(w, ks, vs, 0)
-    print(f"per-token sparse: {res}")
+    res = _check(w, ks, vs, 0, dot)
+    print(f"per-token sparse {dot}: {res}")
 
 
-def test_per_token_decode_benchmark_shape():
+@pytest.mark.parametrize("dot", ["fp8", "bf16"])
+def test_per_token_decode_benchmark_shape(dot):
     w = workloads.make("metric")
     ks, vs = _scales(w, 126)
-    res = _check(w, ks, vs, 0)
-    print(f"per-token metric: {res}")
+    res = _check(w, ks, vs, 0, dot)
+    print(f"per-token metric {dot}: {res}")
 
 
 def test_per_token_quantize_then_decode():
