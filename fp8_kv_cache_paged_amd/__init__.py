@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.mla_fp8_debug_gather.restype = i32
         L.mla_fp8_bench_stream_read.argtypes = [vp, sz, vp, vp]
         L.mla_fp8_bench_stream_read.restype = i32
+        L.mla_fp8_bench_mfma.argtypes = [i32, i32, i32, vp, vp]
+        L.mla_fp8_bench_mfma.restype = i32
         L.mla_fp8_quantize_kv_workspace_size.argtypes = []
         L.mla_fp8_quantize_kv_workspace_size.restype = sz
         L.mla_fp8_quantize_kv.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
@@ -249,6 +251,19 @@ def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     _check(lib().mla_fp8_bench_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), _stream(stream)),
            "mla_fp8_bench_stream_read")
+
+
+def mfma_probe(dot: str, iters: int, blocks: int, sink: torch.Tensor, stream=None) -> int:
+    """Matrix-core throughput probe: blocks x 4 waves, each issuing 4 * iters
+    independent 32x32 MFMAs (dot "fp8": 32x32x64, "bf16": 32x32x16); sink: f32
+    device tensor of >= blocks * 256 elements. Returns the FLOP it executes."""
+    if dot not in ("fp8", "bf16"):
+        raise ValueError(f"dot must be 'fp8' or 'bf16', got {dot!r}")
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < blocks * 256:
+        raise ValueError("sink must be a float32 device tensor of >= blocks * 256 elements")
+    code = MLA_DOT_FP8 if dot == "fp8" else MLA_DOT_BF16
+    _check(lib().mla_fp8_bench_mfma(code, iters, blocks, _ptr(sink), _stream(stream)), "mla_fp8_bench_mfma")
+    return blocks * 4 * iters * 4 * (131072 if dot == "fp8" else 32768)
 
 
 def quantize_kv(ckv: torch.Tensor, k_rope: Optional[torch.Tensor], slot_mapping: torch.Tensor,

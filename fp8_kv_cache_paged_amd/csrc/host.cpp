@@ -302,6 +302,15 @@ MLA_API int32_t mla_fp8_debug_gather(const mla_params* p, const void* kv_cache, 
              : MLA_ERR_HIP;
 }
 
+MLA_API int32_t mla_fp8_bench_mfma(int32_t dot, int32_t iters, int32_t blocks, float* sink, void* hip_stream) {
+  if (sink == nullptr) return MLA_ERR_NULL;
+  if ((dot != MLA_DOT_BF16 && dot != MLA_DOT_FP8) || iters < 1 || blocks < 1) return MLA_ERR_SHAPE;
+  if (!aligned(sink, 4)) return MLA_ERR_ALIGN;
+  return mla::launch_mfma_peak(dot, iters, blocks, sink, static_cast<hipStream_t>(hip_stream)) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 MLA_API int32_t mla_fp8_bench_stream_read(const void* src, size_t bytes, float* sink, void* hip_stream) {
   if (src == nullptr || sink == nullptr) return MLA_ERR_NULL;
   if (bytes % 16 != 0) return MLA_ERR_SHAPE;

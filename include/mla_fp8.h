@@ -216,6 +216,12 @@ MLA_API int32_t mla_fp8_debug_gather(const mla_params* p, const void* kv_cache,
                                      const int32_t* block_table, const int32_t* seq_lens,
                                      void* dense_out, void* hip_stream);
 
+/* Matrix-core throughput probe: `blocks` workgroups of 256 threads, each wave
+ * issuing 4 * iters independent 32x32 MFMAs (MLA_DOT_FP8: 32x32x64 fp8,
+ * 131072 FLOP each; MLA_DOT_BF16: 32x32x16 bf16, 32768 FLOP each) with no
+ * memory traffic; writes one f32 per thread to sink (blocks * 256 floats). */
+MLA_API int32_t mla_fp8_bench_mfma(int32_t dot, int32_t iters, int32_t blocks, float* sink, void* hip_stream);
+
 /* Streams `bytes` (a multiple of 16) of device memory and writes one f32 per
  * workgroup to sink (>= 65536 floats): an HBM read-bandwidth probe. */
 MLA_API int32_t mla_fp8_bench_stream_read(const void* src, size_t bytes, float* sink,

@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
     assert set(names) <= exported
@@ -198,3 +198,16 @@ def test_quantize_workspace_size(L):
 ])
 def test_quantize_host_checks(L, kw, status):
     assert _q(L, **kw) == status
+
+
+def test_mfma_probe_rejects_before_any_launch(L):
+    # host checks only: none of these reaches a kernel launch
+    assert L.mla_fp8_bench_mfma(mla.MLA_DOT_FP8, 4, 4, None, None) == mla.MLA_ERR_NULL
+    assert L.mla_fp8_bench_mfma(7, 4, 4, 256, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_fp8_bench_mfma(mla.MLA_DOT_BF16, 0, 4, 256, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_fp8_bench_mfma(mla.MLA_DOT_FP8, 4, 0, 256, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_fp8_bench_mfma(mla.MLA_DOT_FP8, 4, 4, 258, None) == mla.MLA_ERR_ALIGN
+    with pytest.raises(ValueError):
+        mla.mfma_probe("fp16", 4, 4, torch.empty(1024))
+    with pytest.raises(ValueError):
+        mla.mfma_probe("fp8", 4, 4, torch.empty(1024))   # host tensor
