@@ -76,6 +76,24 @@ def hbm_read_probe(dev, gib=2.0, reps=5):
     return best
 
 
+def mfma_probe(dev, dot, reps=3):
+    """Measured matrix-core throughput (TFLOP/s) with no memory traffic."""
+    blocks, iters = 4096, (2048 if dot == "fp8" else 4096)   # ~3.5 ms per launch
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    mla.mfma_probe(dot, iters, blocks, sink)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flop = mla.mfma_probe(dot, iters, blocks, sink)
+        e1.record(stream)
+        e1.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
+
+
 PROFILE = os.path.join(ROOT, "profiles", "mla_decode_kernel.benchmark_workload.txt")
 
 
@@ -218,6 +236,8 @@ def main():
 
     hbm_meas = hbm_read_probe(dev)
     print(f"[bench] measured HBM read bandwidth {hbm_meas:.0f} GB/s", file=sys.stderr, flush=True)
+    mfma_meas = mfma_probe(dev, args.dot)
+    print(f"[bench] measured {args.dot} matrix-core throughput {mfma_meas:.0f} TFLOP/s", file=sys.stderr, flush=True)
 
     q = torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     bt = torch.from_numpy(w.block_table).to(dev)
@@ -293,6 +313,21 @@ def main():
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
+    # the split kernel's bound: the larger of its HBM floor (its bytes at the HBM
+    # peak) and its matrix-core floor (every FLOP of the call at the dot type's peak)
+    mfma_peak = FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS
+    kernel_name = "mla_decode_kernel" if args.dot == "fp8" else "mla_decode_kernel or mla_decode_rows_kernel"
+    roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,
+                "flop_per_launch": flops}
+    # the committed counter summary covers the benchmark workload's fp8, per-tensor-scale launch only
+    traffic = measured_traffic() if (args.workload == "metric" and args.dot == "fp8" and not per_token) else None
+    if flops / (mfma_peak * 1e12) > kern_bytes / (HBM_PEAK_GBPS * 1e9):
+        kern_tflops = flops / (kern_ms * 1e-3) / 1e12
+        roofline.update({"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                         "frac": round(kern_tflops / mfma_peak, 4), "traffic": traffic})
+    else:
+        roofline.update({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic})
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -316,11 +351,10 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_measured_gbps": round(hbm_meas, 1),
         "frac_of_measured_hbm": round(gbps / hbm_meas, 4),
-        "frac_of_fp8_mfma_peak": round(tflops / (FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS), 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                     "kernel": "mla_decode_kernel", "kernel_us": round(kern_ms * 1e3, 2),
-                     "bytes_per_launch": kern_bytes},
+        "frac_of_mfma_peak": round(tflops / (FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS), 4),
+        "mfma_measured_tflops": round(mfma_meas, 1),
+        "frac_of_measured_mfma": round(tflops / mfma_meas, 4),
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

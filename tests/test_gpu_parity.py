@@ -50,6 +50,24 @@ def test_small_dense(idx, splits, dot):
     print(f"{name}{kw} splits={splits} dot={dot}: {res}")
 
 
+MAXIMA = [
+    # the largest s_q the library takes (a 1024-token causal chunk: 4096 rows, 32 row groups)
+    ("tiny", {"batch": 1, "s_q": 1024, "h_q": 4, "seq_len": [1100], "seed": 27}),
+    # the largest h_q (1024 heads of one token: 8 row groups, ragged 2-page sequence)
+    ("tiny", {"batch": 2, "s_q": 1, "h_q": 1024, "seq_len": [90, 700], "seed": 28}),
+]
+
+
+@pytest.mark.parametrize("dot", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [3, 0])
+@pytest.mark.parametrize("idx", range(len(MAXIMA)))
+def test_maximum_query_tokens_and_heads(idx, splits, dot):
+    name, kw = MAXIMA[idx]
+    w, oc, t = _case(name, **kw)
+    res = gu.check(w, oc, dot, num_splits=splits, t=t)
+    print(f"{name}{kw} splits={splits} dot={dot}: {res}")
+
+
 @pytest.mark.parametrize("dot", ["bf16", "fp8"])
 def test_empty_and_degenerate_rows(dot):
     # sequence lengths 0 and 1 with s_q = 2 (causal): whole sequences and single
