@@ -48,7 +48,7 @@ import math
 
 import numpy as np
 
-from .fp8 import E4M3FN_MAX, bf16_bits_to_f64, decode_e4m3fn, encode_e4m3fn
+from .fp8 import E4M3FN_MAX, bf16_bits_to_f64, decode_e4m3fn, decode_kv_codes, encode_e4m3fn
 
 
 def default_softmax_scale(d_nope: int, d_rope: int) -> float:
@@ -74,13 +74,14 @@ def scale_at(scale, block_table_row, pos, page_block=64):
     return s.reshape(-1, page_block)[pages, pos % page_block]
 
 
-def dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope):
+def dequant_keys_values(rows, k_scale, v_scale, d_nope, d_rope, encoding="e4m3fn"):
     """Cache rows (uint8 [n, row_bytes]) -> K float64 [n, d_nope+d_rope], V [n, d_nope].
 
-    Row layout: d_nope e4m3fn bytes, then d_rope little-endian bf16 values.
-    The scales are scalars or one value per row ([n], see scale_at).
+    Row layout: d_nope one-byte codes (e4m3fn, or gfx942's e4m3fnuz), then
+    d_rope little-endian bf16 values. The scales are scalars or one value per
+    row ([n], see scale_at).
     """
-    nope = decode_e4m3fn(rows[:, :d_nope])
+    nope = decode_kv_codes(rows[:, :d_nope], encoding)
     ks = np.asarray(k_scale, dtype=np.float64)
     vs = np.asarray(v_scale, dtype=np.float64)
     k = nope * (ks[:, None] if ks.ndim else float(ks))
@@ -127,7 +128,7 @@ def query_f64(q_bits, q_nope_override=None, d_nope=512):
 
 def mla_decode(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale, *,
                d_nope=512, d_rope=64, causal=True, softmax_scale=None,
-               indices=None, q_nope_override=None, page_block=64, batches=None):
+               indices=None, q_nope_override=None, page_block=64, batches=None, encoding="e4m3fn"):
     """Attention of every (b, i, h) query row over its visible keys.
 
     Arguments are host arrays in the library's layouts: q_bits uint16 bf16
@@ -137,6 +138,7 @@ def mla_decode(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale, *,
     ``q_nope_override`` (float64 [b, s_q, h_q, d_nope]) replaces the nope part
     of the query; pass the dequantized Q' to get the fp8-dot path's logits.
     ``batches`` restricts the work to those sequence indices (others stay 0).
+    ``encoding`` names the cache's one-byte code ("e4m3fn" or "e4m3fnuz").
 
     Returns out float64 [b, s_q, h_q, d_nope] and lse float64 [b, s_q, h_q].
     """
@@ -152,7 +154,7 @@ def mla_decode(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale, *,
             rows = _positions_to_rows(kv_cache, block_table[b], full, page_block)
             k_all, v_all = dequant_keys_values(rows, scale_at(k_scale, block_table[b], full, page_block),
                                                scale_at(v_scale, block_table[b], full, page_block),
-                                               d_nope, d_rope)
+                                               d_nope, d_rope, encoding)
         for i in range(s_q):
             pos = visible_positions(b, i, seq_lens, s_q, causal, indices)
             if indices is None:
@@ -160,7 +162,8 @@ def mla_decode(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale, *,
             else:
                 rows = _positions_to_rows(kv_cache, block_table[b], pos, page_block)
                 k, v = dequant_keys_values(rows, scale_at(k_scale, block_table[b], pos, page_block),
-                                           scale_at(v_scale, block_table[b], pos, page_block), d_nope, d_rope)
+                                           scale_at(v_scale, block_table[b], pos, page_block), d_nope, d_rope,
+                                           encoding)
             out[b, i], lse[b, i] = _attend(q[b, i], k, v, scale)
     return out, lse
 

@@ -22,7 +22,9 @@ Pinned by tests/test_oracle_fp8.py: anchor codes, a second derivation by bf16
 bit placement (InfiniCore PR #1568, mma kernel commit: placing the code bits in
 bf16 bit positions gives the true value times 2**-120), encode/decode round
 trip, round-half-to-even ties, saturation, and torch's float8_e4m3fn cast as an
-outside library check.
+outside library check. The e4m3fnuz decoder below is pinned the same way:
+torch's float8_e4m3fnuz on all 256 codes, the page's largest value 240, its
+special codes, and the bias identity with e4m3fn on the other 253 codes.
 """
 
 import math
@@ -60,6 +62,54 @@ def decode_e4m3fn(codes) -> np.ndarray:
     if c.dtype != np.uint8:
         c = c.astype(np.uint8)
     return E4M3FN_TABLE[c]
+
+
+# ---- e4m3fnuz (gfx942) -------------------------------------------------------
+# The one-byte float of gfx942 that ROCm/aiter PR #6199 (Technical details)
+# quantizes to, saturating at 240. Its bit fields, from the format's
+# definition:
+#   bit 7 sign, bits 6..3 exponent E with bias 8, bits 2..0 mantissa M
+#   E == 0           subnormal: (M/8) * 2**-7
+#   E in 1..15       normal:    (1 + M/8) * 2**(E-8)   (no NaN among them)
+#   0x80             NaN (the "negative zero" code); 0x00 is the only zero
+# so the largest magnitude is 0x7F = 1.875 * 2**7 = 240 and the smallest
+# subnormal is 2**-10.
+
+E4M3FNUZ_MAX = 240.0
+
+
+def _e4m3fnuz_value(code: int) -> float:
+    """Value of one e4m3fnuz byte, straight from the bit-field definition."""
+    if code == 0x80:
+        return math.nan
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** -7
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 8)
+
+
+#: float64 value of every byte 0..255 (NaN at 0x80 only).
+E4M3FNUZ_TABLE = np.array([_e4m3fnuz_value(c) for c in range(256)], dtype=np.float64)
+E4M3FNUZ_TABLE.setflags(write=False)
+
+
+def decode_e4m3fnuz(codes) -> np.ndarray:
+    """Bytes -> float64 values of the e4m3fnuz encoding (table lookup)."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        c = c.astype(np.uint8)
+    return E4M3FNUZ_TABLE[c]
+
+
+def decode_kv_codes(codes, encoding="e4m3fn") -> np.ndarray:
+    """Cache code bytes -> float64 under the named one-byte encoding."""
+    if encoding == "e4m3fn":
+        return decode_e4m3fn(codes)
+    if encoding == "e4m3fnuz":
+        return decode_e4m3fnuz(codes)
+    raise ValueError(f"unknown encoding {encoding!r}")
 
 
 def encode_e4m3fn(x) -> np.ndarray:

@@ -25,7 +25,9 @@ LSE_TOL = 1e-3
 def device_inputs(w, device="cuda:0"):
     t = {
         "q": torch.from_numpy(w.q_bits.view(np.int16)).view(torch.bfloat16).to(device),
-        "kv": torch.from_numpy(w.kv_cache).to(device),
+        # a uint8 view is read as e4m3fn; an fnuz cache goes in as torch's fnuz dtype
+        "kv": (torch.from_numpy(w.kv_cache).to(device) if w.encoding == "e4m3fn"
+               else torch.from_numpy(w.kv_cache).to(device).view(torch.float8_e4m3fnuz)),
         "bt": torch.from_numpy(w.block_table).to(device),
         "sl": torch.from_numpy(w.seq_lens).to(device),
         "ks": torch.tensor([w.k_scale], dtype=torch.float32, device=device),
@@ -47,7 +49,8 @@ def oracle(w, q_prime=False):
     qo = attn.dequantized_q_nope(w.q_bits, w.d_nope) if q_prime else None
     return attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, w.k_scale, w.v_scale,
                            d_nope=w.d_nope, d_rope=w.d_rope, causal=w.causal,
-                           softmax_scale=w.softmax_scale, indices=w.indices, q_nope_override=qo)
+                           softmax_scale=w.softmax_scale, indices=w.indices, q_nope_override=qo,
+                           encoding=w.encoding)
 
 
 class OracleCache:

@@ -1,0 +1,88 @@
+"""gfx942's e4m3fnuz cache on gfx950.
+
+The cache holds torch float8_e4m3fnuz codes at scale amax/240 (largest fnuz
+value, ROCm/aiter PR #6199, Technical details); the oracle decodes them from
+the fnuz bit fields. Each workload's amax element carries the +-240 codes
+(0x7F / 0xFF, NaN in e4m3fn), and the unowned rows hold 0x80, fnuz's NaN.
+
+The library refuses an fnuz cache in both dot modes (host check, no launch):
+the parity tests below are the bar a kernel that reads it has to meet, and
+stay skipped until one exists.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_paged_amd as mla
+import workloads
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+NOT_BUILT = pytest.mark.skip(reason="e4m3fnuz caches are refused: a bf16-dot kernel variant that decoded them "
+                                    "(e4m3fn convert plus a +-240/NaN fix-up, factor 1/2 on the scales) gave 5% "
+                                    "rel-L2 against the oracle while the e4m3fn kernel on the same bytes with "
+                                    "halved scales matched; cause not found, so the variant was taken out")
+
+CASES = [
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 64, "seq_len": [300, 1], "seed": 121}),
+    ("tiny", {"batch": 3, "s_q": 2, "h_q": 48, "seq_len": [130, 64, 2], "seed": 122}),
+    ("tiny", {"batch": 2, "s_q": 2, "h_q": 16, "d_rope": 0, "seq_len": [257, 90], "seed": 123}),
+    ("sparse", {"batch": 2, "seq_len": 5000, "topk": 300, "seed": 124}),
+]
+_CACHE = {}
+
+
+def _case(name, **kw):
+    key = (name, tuple(sorted((k, str(v)) for k, v in kw.items())))
+    if key not in _CACHE:
+        w = workloads.make(name, encoding="e4m3fnuz", **kw)
+        _CACHE[key] = (w, gu.OracleCache(w), gu.device_inputs(w))
+    return _CACHE[key]
+
+
+def _has_top_codes(w):
+    c = w.kv_cache[..., :w.d_nope]
+    return bool(((c == 0x7F) | (c == 0xFF)).any())
+
+
+@NOT_BUILT
+@pytest.mark.parametrize("splits", [1, 3, 0])
+@pytest.mark.parametrize("idx", range(len(CASES)))
+def test_fnuz_parity_bf16_dots(idx, splits):
+    name, kw = CASES[idx]
+    w, oc, t = _case(name, **kw)
+    assert t["kv"].dtype == torch.float8_e4m3fnuz and _has_top_codes(w)
+    res = gu.check(w, oc, "bf16", num_splits=splits, t=t)
+    print(f"fnuz {name}{kw} splits={splits}: {res}")
+
+
+@NOT_BUILT
+def test_fnuz_full_benchmark_shape_bf16_dots():
+    w, oc, t = _case("metric")
+    res = gu.check(w, oc, "bf16", t=t)
+    print(f"fnuz metric: {res}")
+
+
+@NOT_BUILT
+def test_fnuz_nan_code_poisons_only_the_rows_that_see_it():
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=16, seq_len=[100, 80], encoding="e4m3fnuz", seed=125)
+    page = int(w.block_table[0, 0])
+    w.kv_cache[page, 5, 17] = 0x80            # a visible key of sequence 0 (both its query rows)
+    t = gu.device_inputs(w)
+    out, lse = gu.run(w, t, "bf16", num_splits=1)
+    assert np.isnan(out[0]).all()
+    ref_o, ref_l = gu.oracle(w)
+    assert np.isnan(ref_o[0]).all()
+    gu.compare(out[1:], lse[1:], ref_o[1:], ref_l[1:], dot="bf16")
+
+
+@pytest.mark.parametrize("dot", ["bf16", "fp8"])
+def test_fnuz_cache_is_refused(dot):
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=16, seq_len=[100, 80], encoding="e4m3fnuz", seed=126)
+    t = gu.device_inputs(w)
+    assert t["kv"].dtype == torch.float8_e4m3fnuz
+    with pytest.raises(mla.MlaError) as e:
+        gu.run(w, t, dot, num_splits=1)
+    assert e.value.status == mla.MLA_ERR_UNSUPPORTED

@@ -116,3 +116,47 @@ def test_every_e4m3fn_value_is_exact_in_bf16(code):
     assert fp8.bf16_bits_to_f64(fp8.f32_to_bf16_bits(v)) == v
     allv = fp8.E4M3FN_TABLE[FINITE].astype(np.float32)
     np.testing.assert_array_equal(fp8.bf16_bits_to_f64(fp8.f32_to_bf16_bits(allv)), allv)
+
+
+# ---- e4m3fnuz (gfx942's encoding) ------------------------------------------
+
+
+def test_fnuz_page_fact_largest_value_240():
+    # ROCm/aiter PR #6199 quantizes to 240 for gfx942's fnuz code
+    facts = _anchors()["page_facts"]
+    assert np.nanmax(fp8.E4M3FNUZ_TABLE) == facts[3]["fnuz_max"] == fp8.E4M3FNUZ_MAX
+    assert fp8.E4M3FNUZ_TABLE[0x7F] == 240.0 and fp8.E4M3FNUZ_TABLE[0xFF] == -240.0
+
+
+def test_fnuz_decode_matches_torch_float8_e4m3fnuz():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fnuz).to(torch.float64).numpy()
+    got = fp8.decode_e4m3fnuz(np.arange(256, dtype=np.uint8))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_fnuz_special_codes():
+    t = fp8.E4M3FNUZ_TABLE
+    assert int(np.isnan(t).sum()) == 1 and math.isnan(t[0x80])   # the only NaN
+    assert int((t == 0).sum()) == 1 and not np.signbit(t[0x00])   # no negative zero
+    assert not np.isinf(t).any()
+    assert t[0x01] == 2.0 ** -10                                   # smallest subnormal
+
+
+def test_fnuz_is_half_of_fn_away_from_the_special_codes():
+    # exponent bias 8 instead of 7 with the same bit fields: each code other
+    # than 0x80 (fnuz NaN, fn -0) and 0x7F / 0xFF (fnuz +-240, fn NaN) means
+    # half its e4m3fn value
+    c = np.array([x for x in range(256) if x not in (0x7F, 0x80, 0xFF)], dtype=np.uint8)
+    np.testing.assert_array_equal(fp8.E4M3FNUZ_TABLE[c] * 2.0, fp8.E4M3FN_TABLE[c])
+
+
+def test_kv_code_dispatch():
+    c = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(fp8.decode_kv_codes(c, "e4m3fn"), fp8.E4M3FN_TABLE, equal_nan=True)
+    assert np.array_equal(fp8.decode_kv_codes(c, "e4m3fnuz"), fp8.E4M3FNUZ_TABLE, equal_nan=True)
+    with pytest.raises(ValueError):
+        fp8.decode_kv_codes(c, "e5m2")

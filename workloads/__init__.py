@@ -29,6 +29,9 @@ k_scale = v_scale = that scale. Every byte of the pool that no valid token
 owns (unused pages, the slack of each last page, unreferenced rows of the
 sparse context) is 0xFF, a NaN in both e4m3fn and bf16, so a stray read
 poisons the output. Unused block_table entries point at a poisoned page.
+With ``encoding="e4m3fnuz"`` (gfx942's code, largest value 240) the latent
+is cast to torch's float8_e4m3fnuz at scale amax/240, and the code columns
+of unowned rows are 0x80, that encoding's NaN.
 """
 
 from dataclasses import dataclass, field
@@ -94,6 +97,7 @@ class Workload:
     dots: Tuple[str, ...] = ("fp8",)
     page_block: int = PAGE_BLOCK
     softmax_scale: Optional[float] = None
+    encoding: str = "e4m3fn"      # the cache's one-byte code: e4m3fn or gfx942's e4m3fnuz
     meta: dict = field(default_factory=dict)
 
     @property
@@ -114,16 +118,35 @@ def _bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def _e4m3fn_bytes(x: np.ndarray) -> np.ndarray:
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+#: one-byte cache encodings: torch dtype of the cast, largest magnitude, and
+#: the byte that poisons the code columns (a NaN of the encoding)
+ENCODINGS = {"e4m3fn": (torch.float8_e4m3fn, 448.0, 0xFF),
+             "e4m3fnuz": (torch.float8_e4m3fnuz, 240.0, 0x80)}
+
+
+def _code_bytes(x: np.ndarray, encoding: str) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(ENCODINGS[encoding][0])
     return t.view(torch.uint8).numpy()
 
 
-def _per_tensor_scale(latent: np.ndarray) -> np.float32:
+def _per_tensor_scale(latent: np.ndarray, qmax: float = 448.0) -> np.float32:
     amax = np.float32(np.abs(latent).max()) if latent.size else np.float32(0)
     if amax == 0:
         return np.float32(1.0)
-    return np.float32(amax / np.float32(448.0))
+    return np.float32(amax / np.float32(qmax))
+
+
+def _encode_latent(latent: np.ndarray, spec) -> Tuple[np.ndarray, np.float32]:
+    """Per-tensor scale (amax / the encoding's largest value) and the codes."""
+    enc = spec.get("encoding", "e4m3fn")
+    scale = _per_tensor_scale(latent, ENCODINGS[enc][1])
+    return _code_bytes(latent / scale, enc), scale
+
+
+def _poisoned_pool(pool: int, row_bytes: int, d_nope: int, spec) -> np.ndarray:
+    cache = np.full((pool, PAGE_BLOCK, row_bytes), POISON, dtype=np.uint8)
+    cache[:, :, :d_nope] = ENCODINGS[spec.get("encoding", "e4m3fn")][2]
+    return cache
 
 
 def make(name: str, seed: Optional[int] = None, **overrides) -> Workload:
@@ -171,14 +194,13 @@ def _make_dense(name, spec, rng) -> Workload:
     ntok = int(seq_lens.sum())
     latent = rng.standard_normal((ntok, d_nope), dtype=np.float32)
     rope = rng.standard_normal((ntok, d_rope), dtype=np.float32)
-    scale = _per_tensor_scale(latent)
-    codes = _e4m3fn_bytes(latent / scale)
+    codes, scale = _encode_latent(latent, spec)
     del latent
     rope_bytes = _bf16_bits(rope).view(np.uint8).reshape(ntok, 2 * d_rope)
     pages_per_seq = -(-seq_lens.astype(np.int64) // PAGE_BLOCK)
     bt, pool = _page_pool(rng, pages_per_seq, spec.get("extra_pages", 2))
     row_bytes = d_nope + 2 * d_rope
-    cache = np.full((pool, PAGE_BLOCK, row_bytes), POISON, dtype=np.uint8)
+    cache = _poisoned_pool(pool, row_bytes, d_nope, spec)
     t0 = 0
     for bi in range(b):
         n = int(seq_lens[bi])
@@ -195,7 +217,8 @@ def _make_dense(name, spec, rng) -> Workload:
                     causal=bool(spec["causal"]), topk=0, q_bits=q_bits, kv_cache=cache,
                     block_table=bt, seq_lens=seq_lens, k_scale=float(scale),
                     v_scale=float(scale), num_splits=spec.get("num_splits", 0),
-                    dots=tuple(spec["dots"]), softmax_scale=spec.get("softmax_scale"))
+                    dots=tuple(spec["dots"]), softmax_scale=spec.get("softmax_scale"),
+                    encoding=spec.get("encoding", "e4m3fn"))
 
 
 def _make_sparse(name, spec, rng) -> Workload:
@@ -230,13 +253,12 @@ def _make_sparse(name, spec, rng) -> Workload:
             else:
                 q[bi, i] = noise[bi, i]
     q_bits = _bf16_bits(q)
-    scale = _per_tensor_scale(latent)
-    codes = _e4m3fn_bytes(latent / scale)
+    codes, scale = _encode_latent(latent, spec)
     rope_bytes = _bf16_bits(rope).view(np.uint8).reshape(nref, 2 * d_rope)
     pages_per_seq = -(-seq_lens.astype(np.int64) // PAGE_BLOCK)
     bt, pool = _page_pool(rng, pages_per_seq, spec.get("extra_pages", 2))
     row_bytes = d_nope + 2 * d_rope
-    cache = np.full((pool, PAGE_BLOCK, row_bytes), POISON, dtype=np.uint8)
+    cache = _poisoned_pool(pool, row_bytes, d_nope, spec)
     for bi in range(b):
         pos = ref[bi].astype(np.int64)
         pages = bt[bi, pos // PAGE_BLOCK]
@@ -249,7 +271,8 @@ def _make_sparse(name, spec, rng) -> Workload:
                     block_table=bt, seq_lens=seq_lens, k_scale=float(scale),
                     v_scale=float(scale), indices=indices,
                     num_splits=spec.get("num_splits", 0), dots=tuple(spec["dots"]),
-                    softmax_scale=spec.get("softmax_scale"))
+                    softmax_scale=spec.get("softmax_scale"),
+                    encoding=spec.get("encoding", "e4m3fn"))
 
 
 def flops(w: Workload) -> float:
