@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--scales", default="tensor", choices=["tensor", "token"],
                     help="per-tensor k/v scales, or one per cache row (fp8 dots, dense)")
+    ap.add_argument("--kv-encoding", default="e4m3fn", choices=["e4m3fn", "e4m3fnuz"],
+                    help="the cache's one-byte code (gfx942's e4m3fnuz: bf16 dots, per-tensor scales)")
     ap.add_argument("--op", default="decode", choices=["decode", "quantize"],
                     help="decode (the benchmark) or the quantize-on-write of the benchmark's cache")
     return ap.parse_args()
@@ -131,7 +133,7 @@ def cpu_baseline(w, budget_s):
         t0 = time.perf_counter()
         attn.mla_decode(sub.q_bits, sub.kv_cache, sub.block_table, sub.seq_lens, sub.k_scale, sub.v_scale,
                         d_nope=sub.d_nope, d_rope=sub.d_rope, causal=sub.causal, indices=sub.indices,
-                        softmax_scale=sub.softmax_scale)
+                        softmax_scale=sub.softmax_scale, encoding=sub.encoding)
         t_used += time.perf_counter() - t0
         flops_done += workloads.flops(sub)
         seqs += 1
@@ -228,7 +230,7 @@ def main():
     if args.op == "quantize":
         return main_quantize(args, dev, hbm_read_probe(dev))
 
-    w = workloads.make(args.workload)
+    w = workloads.make(args.workload, encoding=args.kv_encoding)
     flops = workloads.flops(w)
     nbytes = workloads.algorithmic_bytes(w)
     print(f"[bench] workload {args.workload}: b={w.batch} s_q={w.s_q} h_q={w.h_q} d_rope={w.d_rope} "
@@ -254,6 +256,9 @@ def main():
     kv0 = torch.from_numpy(w.kv_cache).to(dev)
     copies = max(1, int(np.ceil(args.rotate_bytes * (1 << 30) / kv0.numel())))
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    if args.kv_encoding == "e4m3fnuz":   # the library reads the encoding from the tensor's dtype
+        kvs = [k.view(torch.float8_e4m3fnuz) for k in kvs]
+        kv0 = kvs[0]
     out = torch.empty((w.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
     p = mla.params_for(q, kv0, bt, causal=w.causal, dot=args.dot, indices=idx, per_token_scales=per_token)
@@ -320,7 +325,8 @@ def main():
     roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,
                 "flop_per_launch": flops}
     # the committed counter summary covers the benchmark workload's fp8, per-tensor-scale launch only
-    traffic = measured_traffic() if (args.workload == "metric" and args.dot == "fp8" and not per_token) else None
+    traffic = (measured_traffic() if (args.workload == "metric" and args.dot == "fp8" and not per_token
+                                      and args.kv_encoding == "e4m3fn") else None)
     if flops / (mfma_peak * 1e12) > kern_bytes / (HBM_PEAK_GBPS * 1e9):
         kern_tflops = flops / (kern_ms * 1e-3) / 1e12
         roofline.update({"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
@@ -346,7 +352,7 @@ def main():
                                f"page=64 {'causal' if w.causal else 'non-causal'}"
                                + (f" topk={w.topk}" if w.topk else ""),
                    "dots": args.dot, "splits": splits, "kv_copies_rotated": copies,
-                   "scales": "per token" if per_token else "per tensor"},
+                   "scales": "per token" if per_token else "per tensor", "kv_encoding": args.kv_encoding},
         "ms_per_call": round(ms_per_step, 5),
         "hbm_gbps": round(gbps, 1),
         "hbm_measured_gbps": round(hbm_meas, 1),

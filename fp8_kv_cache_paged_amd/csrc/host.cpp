@@ -40,6 +40,9 @@ int32_t validate(const mla_params* p) {
     case MLA_KV_UINT8:
       break;
     case MLA_KV_FP8_E4M3FNUZ:
+      // decoded to bf16 in registers; the fp8 matrix cores read OCP codes only
+      if (p->dot != MLA_DOT_BF16 || p->kv_scale_per_token != 0) return MLA_ERR_UNSUPPORTED;
+      break;
     case MLA_KV_FP8_E5M2:
     case MLA_KV_INT8:
     case MLA_KV_BF16:
@@ -166,6 +169,7 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   const char* rk = getenv("MLA_FP8_ROWS_KERNEL");
   d.rows_kernel = rk != nullptr && rk[0] == '1';
   d.per_token = p->kv_scale_per_token != 0;
+  d.fnuz = p->kv_dtype == MLA_KV_FP8_E4M3FNUZ;
   const char* dbg = getenv("MLA_FP8_DEBUG");
   d.debug_print = dbg != nullptr && dbg[0] == '1';
   if (d.debug_print)

@@ -82,6 +82,27 @@ __device__ inline i32x2 fp8x4_to_bf16x4(int v) {
   return i32x2{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
 }
 
+// Cache bytes -> bf16 for the bf16-dot path. e4m3fn: the converter, exact.
+// FNUZ (gfx942's e4m3fnuz: exponent bias 8, largest magnitude 240, NaN only
+// at 0x80; ROCm/aiter PR #6199, Technical details): each code's sign goes to
+// bf16 bit 15 and its exponent and mantissa bits to bits 10..4, which gives
+// the fnuz value times 2^-119 for every code (the subnormal codes become
+// bf16 subnormals; +-240 needs no special case); the kernel multiplies the k
+// and v scales by 2^119. 0x80, fnuz's NaN, reads as zero.
+constexpr int kFnuzExp = 119;
+template <bool FNUZ>
+__device__ inline i32x2 kv_bytes_to_bf16x4(int v) {
+  if constexpr (FNUZ) {
+    const unsigned u = (unsigned)v;
+    const unsigned x = (u & 0xffu) | ((u & 0xff00u) << 8);           // bytes 0, 1 at bits 0, 16
+    const unsigned y = ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u);  // bytes 2, 3
+    const unsigned bx = ((x & 0x007f007fu) << 4) | ((x & 0x00800080u) << 8);
+    const unsigned by = ((y & 0x007f007fu) << 4) | ((y & 0x00800080u) << 8);
+    return i32x2{(int)bx, (int)by};
+  }
+  return fp8x4_to_bf16x4(v);
+}
+
 // 4 floats -> 4 packed e4m3fn bytes (round to nearest even).
 __device__ inline int f32x4_to_fp8x4(float a, float b, float c, float d) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -702,11 +723,13 @@ template <> struct Soft<0> { static constexpr float tau = 8.f, ps_log2 = 0.f; };
 // the 64 rows' k- and v-scales into LDS; the nope sums are multiplied by their
 // key's k-scale, and p by its key's v-scale before the bf16 packing (bf16 has
 // the range, so no reference scale is needed).
-template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V, bool PT = false>
+// FNUZ: the cache holds gfx942's e4m3fnuz codes (bf16 dots, per-tensor scales).
+template <int DOT, int ROPE, bool SPARSE, int NW, bool GATHER_V, bool PT = false, bool FNUZ = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1)))
 void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   static_assert(!(PT && DOT == DOT_FP8), "per-token scales with fp8 dots use the dv-split kernel");
+  static_assert(!(FNUZ && (DOT == DOT_FP8 || PT || GATHER_V)), "fnuz codes: bf16 dots, per-tensor scales");
   constexpr int D = kNope + ROPE;               // q row length
   __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + (PT ? kBufs * 512 : 0)];
   uint8_t* const lds = lds_;
@@ -815,7 +838,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
       stage_q_fp8(qrow, row_ok && wave_active, h, qn, e);
       qk_scale = ldexpf(ks, e);
     } else {
-      qk_scale = ks;
+      qk_scale = FNUZ ? ldexpf(ks, kFnuzExp) : ks;   // fnuz codes decode to 2^-119 times their value
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
         const int d0 = 32 * (u >> 1) + 16 * h + 8 * (u & 1);
@@ -955,8 +978,8 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         if (f + PD < NI) load(f + PD);
         if (f < NN) {
           const int t = f >> 1;
-          const i32x2 b0 = fp8x4_to_bf16x4(raw.x), b1 = fp8x4_to_bf16x4(raw.y);
-          const i32x2 b2 = fp8x4_to_bf16x4(raw.z), b3 = fp8x4_to_bf16x4(raw.w);
+          const i32x2 b0 = kv_bytes_to_bf16x4<FNUZ>(raw.x), b1 = kv_bytes_to_bf16x4<FNUZ>(raw.y);
+          const i32x2 b2 = kv_bytes_to_bf16x4<FNUZ>(raw.z), b3 = kv_bytes_to_bf16x4<FNUZ>(raw.w);
           const bf16x8 a0 = __builtin_bit_cast(bf16x8, i32x4{b0.x, b0.y, b1.x, b1.y});
           const bf16x8 a1 = __builtin_bit_cast(bf16x8, i32x4{b2.x, b2.y, b3.x, b3.y});
           if (f < 2) mfma_bf16_pair_first_after_valu(Sn[kb], a0, qb[2 * t], a1, qb[2 * t + 1]);
@@ -1128,7 +1151,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         if (blk + PDV < 16) vr[blk % PDV] = vfrag(blk + PDV);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const i32x2 lo = fp8x4_to_bf16x4(cur[2 * u]), hi = fp8x4_to_bf16x4(cur[2 * u + 1]);
+          const i32x2 lo = kv_bytes_to_bf16x4<FNUZ>(cur[2 * u]), hi = kv_bytes_to_bf16x4<FNUZ>(cur[2 * u + 1]);
           const bf16x8 av = __builtin_bit_cast(bf16x8, i32x4{lo.x, lo.y, hi.x, hi.y});
           mfma_bf16_32x32x16_acc(O[blk], av, pb[u]);
         }
@@ -1153,7 +1176,8 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   const bool nonempty = l_tot > 0.f;
   // splits == 1: the output, scaled by v_scale; else the partials, normalized
   // by the row sum only (fp16, |value| <= 448; the combine applies v_scale)
-  const float inv = nonempty ? (PT ? 1.f : (a.splits == 1 ? *v_scale : 1.f)) / l_tot : 0.f;
+  // (fnuz: V decoded to 2^-119 times its value, restored here)
+  const float inv = nonempty ? ldexpf(PT ? 1.f : (a.splits == 1 ? *v_scale : 1.f), FNUZ ? kFnuzExp : 0) / l_tot : 0.f;
   const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
 
   if (a.splits == 1) {
@@ -2024,6 +2048,18 @@ static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t s
                                    st, MLA_PTR_ARGS(d), a); break;
         default: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 4, false, true>), grid, dim3(256), 0,
                                     st, MLA_PTR_ARGS(d), a); break;
+      }
+      return hipGetLastError();
+    }
+    if (d.fnuz) {
+      const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
+      switch (waves_per_group(d.row_blocks)) {
+        case 1: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 1, false, false, true>), grid,
+                                   dim3(64), 0, st, MLA_PTR_ARGS(d), a); break;
+        case 2: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 2, false, false, true>), grid,
+                                   dim3(128), 0, st, MLA_PTR_ARGS(d), a); break;
+        default: hipLaunchKernelGGL((mla_decode_rows_kernel<DOT, ROPE, SPARSE, 4, false, false, true>), grid,
+                                    dim3(256), 0, st, MLA_PTR_ARGS(d), a); break;
       }
       return hipGetLastError();
     }

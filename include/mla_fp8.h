@@ -78,12 +78,18 @@ extern "C" {
 #define MLA_ERR_ALIGN 6        /* a pointer is not aligned as required */
 #define MLA_ERR_HIP 7          /* the HIP runtime reported an error */
 
-/* kv_dtype codes. Only the OCP e4m3fn encoding (or a uint8 view of it) is
- * read; the other one-byte encodings are refused rather than misread
- * (ROCm/aiter PR #6199, the foreign-encoding refusal commit). */
+/* kv_dtype codes. The OCP e4m3fn encoding (or a uint8 view of it) is read
+ * by both dot modes. gfx942's e4m3fnuz (bias 8, largest magnitude 240, NaN
+ * only at 0x80; ROCm/aiter PR #6199, Technical details) is read with
+ * MLA_DOT_BF16 and per-tensor scales only: its codes are decoded exactly to
+ * bf16 in registers (0x80, the NaN code, reads as zero), while the fp8
+ * matrix cores read OCP codes only (MLA_DOT_FP8 or per-token scales with an
+ * fnuz cache is MLA_ERR_UNSUPPORTED). The other one-byte encodings are
+ * refused rather than misread (ROCm/aiter PR #6199, the foreign-encoding
+ * refusal commit). */
 #define MLA_KV_FP8_E4M3FN 0
 #define MLA_KV_UINT8 1          /* raw bytes, taken to be e4m3fn */
-#define MLA_KV_FP8_E4M3FNUZ 2   /* refused: MLA_ERR_UNSUPPORTED */
+#define MLA_KV_FP8_E4M3FNUZ 2   /* bf16 dots, per-tensor scales; else MLA_ERR_UNSUPPORTED */
 #define MLA_KV_FP8_E5M2 3       /* refused: MLA_ERR_UNSUPPORTED */
 #define MLA_KV_INT8 4           /* refused: MLA_ERR_UNSUPPORTED */
 #define MLA_KV_BF16 5           /* refused: MLA_ERR_UNSUPPORTED */

@@ -52,7 +52,9 @@ def good(**kw):
 @pytest.mark.parametrize("kw,status", [
     ({}, mla.MLA_OK),
     ({"kv_dtype": torch.float8_e4m3fn}, mla.MLA_OK),
-    ({"kv_dtype": torch.float8_e4m3fnuz}, mla.MLA_ERR_UNSUPPORTED),
+    ({"kv_dtype": torch.float8_e4m3fnuz}, mla.MLA_ERR_UNSUPPORTED),            # fp8 dots (the default)
+    ({"kv_dtype": torch.float8_e4m3fnuz, "dot": "bf16"}, mla.MLA_OK),           # decoded to bf16 in registers
+    ({"kv_dtype": torch.float8_e4m3fnuz, "dot": "bf16", "per_token_scales": True}, mla.MLA_ERR_UNSUPPORTED),
     ({"kv_dtype": torch.float8_e5m2}, mla.MLA_ERR_UNSUPPORTED),
     ({"kv_dtype": torch.int8}, mla.MLA_ERR_UNSUPPORTED),
     ({"kv_dtype": torch.bfloat16}, mla.MLA_ERR_UNSUPPORTED),
