@@ -34,6 +34,19 @@ FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0
 
 
+def split_kernel_bytes(nbytes, splits):
+    """Algorithmic bytes the split kernel is responsible for: KV rows, Q and the
+    tables; out and lse too when there is one split (else the combine writes them)."""
+    return nbytes["kv"] + nbytes["q"] + nbytes["tables"] + (0 if splits > 1 else nbytes["out"] + nbytes["lse"])
+
+
+def split_kernel_bound(flops, kern_bytes, dot):
+    """The larger of the kernel's two floors: its bytes at the HBM peak, or the
+    call's FLOPs at the dot type's MFMA peak."""
+    mfma_peak = FP8_PEAK_TFLOPS if dot == "fp8" else BF16_PEAK_TFLOPS
+    return "mfma" if flops / (mfma_peak * 1e12) > kern_bytes / (HBM_PEAK_GBPS * 1e9) else "hbm"
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,7 +229,8 @@ def main_quantize(args, dev, hbm_meas):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 (sequences shard across "
+                                   "GPUs with no exchange, so N GPUs run N copies of this workload)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -312,14 +326,10 @@ def main():
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in durs]))
     assert torch.isfinite(out.float()).all(), "non-finite output"
 
-    # bytes the split kernel is responsible for: KV rows, Q, tables; out/lse are
-    # written by the combine when splits > 1
-    kern_bytes = nbytes["kv"] + nbytes["q"] + nbytes["tables"] + (0 if splits > 1 else nbytes["out"] + nbytes["lse"])
+    kern_bytes = split_kernel_bytes(nbytes, splits)
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
-    # the split kernel's bound: the larger of its HBM floor (its bytes at the HBM
-    # peak) and its matrix-core floor (every FLOP of the call at the dot type's peak)
     mfma_peak = FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS
     kernel_name = "mla_decode_kernel" if args.dot == "fp8" else "mla_decode_kernel or mla_decode_rows_kernel"
     roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,
@@ -327,7 +337,7 @@ def main():
     # the committed counter summary covers the benchmark workload's fp8, per-tensor-scale launch only
     traffic = (measured_traffic() if (args.workload == "metric" and args.dot == "fp8" and not per_token
                                       and args.kv_encoding == "e4m3fn") else None)
-    if flops / (mfma_peak * 1e12) > kern_bytes / (HBM_PEAK_GBPS * 1e9):
+    if split_kernel_bound(flops, kern_bytes, args.dot) == "mfma":
         kern_tflops = flops / (kern_ms * 1e-3) / 1e12
         roofline.update({"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                          "frac": round(kern_tflops / mfma_peak, 4), "traffic": traffic})
