@@ -94,10 +94,13 @@ template <bool FNUZ>
 __device__ inline i32x2 kv_bytes_to_bf16x4(int v) {
   if constexpr (FNUZ) {
     const unsigned u = (unsigned)v;
-    const unsigned x = (u & 0xffu) | ((u & 0xff00u) << 8);           // bytes 0, 1 at bits 0, 16
-    const unsigned y = ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u);  // bytes 2, 3
-    const unsigned bx = ((x & 0x007f007fu) << 4) | ((x & 0x00800080u) << 8);
-    const unsigned by = ((y & 0x007f007fu) << 4) | ((y & 0x00800080u) << 8);
+    // v_perm_b32 byte selects (selector 0..3: a byte of the second source,
+    // 0x0C: zero): bytes 0, 1 to bits 0, 16; bytes 2, 3 likewise
+    const unsigned x = __builtin_amdgcn_perm(0u, u, 0x0c010c00u);
+    const unsigned y = __builtin_amdgcn_perm(0u, u, 0x0c030c02u);
+    const unsigned tx = x << 4, ty = y << 4;   // exponent and mantissa at bits 10..4, sign at bit 11
+    const unsigned bx = (tx & 0x07f007f0u) | ((tx << 4) & 0x80008000u);
+    const unsigned by = (ty & 0x07f007f0u) | ((ty << 4) & 0x80008000u);
     return i32x2{(int)bx, (int)by};
   }
   return fp8x4_to_bf16x4(v);
