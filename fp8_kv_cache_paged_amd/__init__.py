@@ -7,7 +7,6 @@ eager fallback: if the library is missing, every entry point raises.
 """
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -38,6 +37,11 @@ MLA_KV_BF16 = 5
 MLA_DOT_BF16 = 0
 MLA_DOT_FP8 = 1
 MLA_MAX_SPLITS = 64
+
+# kernel variants of the test-only decode export
+MLA_VARIANT_GATHER_V = 1
+MLA_VARIANT_ROWS = 2
+MLA_VARIANT_DV_SPLIT = 4
 
 _KV_DTYPES = {
     torch.float8_e4m3fn: MLA_KV_FP8_E4M3FN,
@@ -91,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.mla_fp8_decode.restype = i32
         L.mla_fp8_decode_partials.argtypes = dec_args
         L.mla_fp8_decode_partials.restype = i32
+        L.mla_fp8_debug_decode_variant.argtypes = dec_args[:-1] + [i32, vp]
+        L.mla_fp8_debug_decode_variant.restype = i32
         L.mla_fp8_status_string.argtypes = [i32]
         L.mla_fp8_status_string.restype = ctypes.c_char_p
         L.mla_fp8_debug_decode_e4m3fn.argtypes = [vp, vp, vp, i32, vp]
@@ -181,12 +187,14 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
            causal: bool = True, softmax_scale: float = 0.0, indices: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, stream=None,
-           partials_only: bool = False, per_token_scales: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+           partials_only: bool = False, per_token_scales: bool = False,
+           variant: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """MLA decode over the paged fp8 cache; returns (out bf16 [b,s_q,h_q,512], lse f32 [b,s_q,h_q]).
 
     q bf16 [b, s_q, h_q, 576|512]; kv_cache uint8/float8_e4m3fn [pages, 64, (1,) 640|512];
     block_table, seq_lens int32; k_scale, v_scale f32 device tensors of one element;
-    indices int32 [b, s_q, topk] selects the sparse variant.
+    indices int32 [b, s_q, topk] selects the sparse variant. ``variant`` (tests
+    only) forces an internal kernel variant, MLA_VARIANT_* bits.
     """
     p = params_for(q, kv_cache, block_table, causal=causal, dot=dot, indices=indices,
                    softmax_scale=softmax_scale, per_token_scales=per_token_scales)
@@ -204,10 +212,16 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
     need = L.mla_fp8_decode_workspace_size(ctypes.byref(p), splits) if splits > 0 else 0
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    fn = L.mla_fp8_decode_partials if partials_only else L.mla_fp8_decode
-    st = fn(ctypes.byref(p), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(k_scale),
+    args = (ctypes.byref(p), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(k_scale),
             _ptr(v_scale), int(splits), _ptr(out), _ptr(lse), _ptr(indices), _ptr(workspace),
-            0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+            0 if workspace is None else workspace.numel() * workspace.element_size())
+    if variant:
+        if partials_only:
+            raise ValueError("variant and partials_only cannot be combined")
+        st = L.mla_fp8_debug_decode_variant(*args, int(variant), _stream(stream))
+    else:
+        fn = L.mla_fp8_decode_partials if partials_only else L.mla_fp8_decode
+        st = fn(*args, _stream(stream))
     _check(st, "mla_fp8_decode")
     return out, lse
 
@@ -299,7 +313,3 @@ def quantize_kv(ckv: torch.Tensor, k_rope: Optional[torch.Tensor], slot_mapping:
                                      _ptr(slot_mapping), _ptr(kv_cache), _ptr(k_scale), _ptr(v_scale),
                                      mode, _ptr(workspace), ws_bytes, _stream(stream)),
            "mla_fp8_quantize_kv")
-
-
-def default_softmax_scale(d_nope: int = 512, d_rope: int = 64) -> float:
-    return 1.0 / math.sqrt(d_nope + d_rope)

@@ -111,7 +111,7 @@ int32_t device_cu_count() {
 int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
                     const int32_t* seq_lens, const float* k_scale, const float* v_scale, int32_t num_splits,
                     void* out, float* lse, const int32_t* indices, void* ws, size_t ws_bytes, void* stream,
-                    bool with_combine) {
+                    bool with_combine, int32_t variant) {
   int32_t st = validate(p);
   if (st != MLA_OK) return st;
   if (q == nullptr || kv_cache == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr ||
@@ -164,10 +164,9 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   d.part_o = need > 0 ? static_cast<uint16_t*>(ws) : nullptr;
   d.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + frags * 16 * 64 * 16 * sizeof(uint16_t))
                         : nullptr;
-  const char* gv = getenv("MLA_FP8_GATHER_V");
-  d.gather_v = gv != nullptr && gv[0] == '1';
-  const char* rk = getenv("MLA_FP8_ROWS_KERNEL");
-  d.rows_kernel = rk != nullptr && rk[0] == '1';
+  d.gather_v = (variant & MLA_VARIANT_GATHER_V) != 0;
+  d.rows_kernel = (variant & MLA_VARIANT_ROWS) != 0;
+  d.dv_split_kernel = (variant & MLA_VARIANT_DV_SPLIT) != 0;
   d.per_token = p->kv_scale_per_token != 0;
   d.fnuz = p->kv_dtype == MLA_KV_FP8_E4M3FNUZ;
   const char* dbg = getenv("MLA_FP8_DEBUG");
@@ -207,7 +206,17 @@ MLA_API int32_t mla_fp8_decode(const mla_params* p, const void* q, const void* k
                                const int32_t* indices, void* workspace_ptr, size_t workspace_bytes,
                                void* hip_stream) {
   return decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
-                     workspace_ptr, workspace_bytes, hip_stream, true);
+                     workspace_ptr, workspace_bytes, hip_stream, true, 0);
+}
+
+MLA_API int32_t mla_fp8_debug_decode_variant(const mla_params* p, const void* q, const void* kv_cache,
+                                             const int32_t* block_table, const int32_t* seq_lens,
+                                             const float* k_scale, const float* v_scale, int32_t num_splits,
+                                             void* out, float* lse, const int32_t* indices, void* workspace_ptr,
+                                             size_t workspace_bytes, int32_t variant, void* hip_stream) {
+  if (variant & ~(MLA_VARIANT_GATHER_V | MLA_VARIANT_ROWS | MLA_VARIANT_DV_SPLIT)) return MLA_ERR_SHAPE;
+  return decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
+                     workspace_ptr, workspace_bytes, hip_stream, true, variant);
 }
 
 MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, const void* kv_cache,
@@ -216,7 +225,7 @@ MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, cons
                                         void* out, float* lse, const int32_t* indices, void* workspace_ptr,
                                         size_t workspace_bytes, void* hip_stream) {
   return decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
-                     workspace_ptr, workspace_bytes, hip_stream, false);
+                     workspace_ptr, workspace_bytes, hip_stream, false, 0);
 }
 
 MLA_API const char* mla_fp8_status_string(int32_t status) {

@@ -30,6 +30,7 @@ struct DecodeLaunch {
   float softmax_scale;
   bool gather_v;       // debug: byte-gather V^T fragments instead of transposed LDS reads
   bool rows_kernel;    // fp8 dots: P.V split by row block (as for bf16 dots) instead of by dv
+  bool dv_split_kernel;  // fp8 dots: the four-wave dv-split kernel instead of the default
   bool per_token;      // k_scale, v_scale: one per cache row ([num_pages, 64])
   bool fnuz;           // e4m3fnuz cache codes (bf16 dots, per-tensor scales)
   bool debug_print;

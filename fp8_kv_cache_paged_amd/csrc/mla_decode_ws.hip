@@ -1,0 +1,520 @@
+// FP8-dot paged MLA decode with role-split waves, three per SIMD (gfx950).
+//
+// What is computed is the decode of mla_decode.hip (FlashMLA PR #82 "update fp8
+// support", description; ROCm/aiter PR #6199, Technical details; InfiniCore
+// PR #1568, Summary and split-kv commit): softmax attention of every query
+// row of a sequence over its paged e4m3fn latent cache, K = [nope * k_scale,
+// bf16 rope], V = nope * v_scale, with Q's nope part quantized per row to
+// e4m3fn and P to e4m3fn for the fp8 matrix cores.
+//
+// Why another kernel: with all 128 query rows of a sequence in one workgroup,
+// the fp32 output accumulator O (128 rows x 512 dv) takes 256 registers per
+// lane at one wave per SIMD, and a lone wave issues its MFMAs, its LDS reads
+// and its softmax VALU work one after another. Here the work of a tile is
+// split by role over twelve waves, three per SIMD, so that one wave's
+// softmax and LDS waits overlap another's matrix products:
+//  * waves 0..3 ("S-waves"): wave r owns query rows 32r..32r+31 of the row
+//    group; S^T = K Q^T of the tile (16 fp8 and 8 bf16 32x32 MFMAs), the
+//    masked online softmax in the log2 domain, and P^T of the tile to LDS;
+//  * waves 4..11 ("PV-waves"): wave 4+e owns dv 64e..64e+63 of all 128 rows,
+//    O^T += V^T P^T (8 fp8 32x32x64 MFMAs per tile, O in 128 VGPRs), and
+//    issues one eighth of the tile copies (global -> LDS).
+// The PV-waves multiply tile k-1 while the S-waves take tile k; one barrier
+// per tile orders the three-tile LDS ring, the P^T exchange (double-buffered
+// by tile parity) and the rescale flags. S-wave r and PV-waves r, r+4 share
+// SIMD r (waves are placed on the SIMDs round-robin). During its S^T
+// products an S-wave runs at raised priority, so the P.V products fill the
+// matrix core around them rather than delaying them.
+//
+// The tile layout in LDS (XOR-swizzled 16-byte chunks), the fragment
+// bookkeeping of the 32x32 MFMAs, the fp8 query quantization, the lazily
+// raised running max and the P scale are those of mla_decode.hip
+// (mla_device.h); the two kernels issue the same products and agree to
+// rounding order.
+
+#include "mla_device.h"
+
+namespace mla {
+
+constexpr int kSWaves = 4;     // one per 32-row block of the row group
+constexpr int kPVWaves = 8;    // one per 64-wide dv slice
+constexpr int kWsThreads = 64 * (kSWaves + kPVWaves);
+
+// LDS past the KV ring, double-buffered by tile parity: P^T of the four row
+// blocks (2 KiB each, two 16-byte halves per lane), per-row rescale factors
+// and per-row-block flags; then the per-row output scale for the epilogue.
+struct WsX {
+  static constexpr int p_bytes = kSWaves * 2048;
+  static constexpr int alpha_bytes = kSWaves * 32 * 4;
+  static constexpr int flag_off = 2 * p_bytes + 2 * alpha_bytes;   // 2 x 4 ints
+  static constexpr int fin_off = flag_off + 32;
+  static constexpr int bytes = fin_off + kSWaves * 32 * 4;
+};
+
+// Max of x over lanes l and l ^ 32 (the two halves of one query row) with the
+// gfx950 lane swap: no LDS round trip.
+__device__ inline float pair_max_swap(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum_swap(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The tile copies of PV-wave e: nope copies 4e..4e+3 (rows 2c, 2c+1 each) and
+// rope copy e (rows 8e..8e+7). Lane l of nope copy c moves the chunk at
+// position l % 32 of row 2c + l / 32, i.e. global chunk (l % 32) ^ (row & 15);
+// lane l of rope copy r the chunk at position l % 8 of row 8r + l / 8, i.e.
+// global chunk (l % 8) ^ ((row >> 1) & 7). A full page is copied with the
+// scalar page base; rows at or past `valid` are zero-filled instead (the
+// page's slack, or the whole tile for a missing page), and the wave then
+// drains its copies so that its zero stores and copies land together.
+template <int ROPE>
+__device__ __attribute__((always_inline)) inline void ws_issue_tile(uint8_t* lds, int bufi, const uint8_t* page_base,
+                                                                    int valid, int e) {
+  constexpr int RB = kNope + 2 * ROPE;
+  int lane;   // volatile: recomputed here rather than kept across the tile loop
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int hi = lane >> 5, p = lane & 31, r8 = lane >> 3, p8 = lane & 7;
+  uint8_t* nope = lds + bufi * kNopeRegion;
+  uint8_t* rope = lds + kRopeBase + bufi * kRopeRegion;
+  if (valid == kKeys) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * e + i;
+      // (2c + hi) & 15 = 2 (c & 7) + hi: the lane part is (p ^ hi) << 4 xor 32 (c & 7)
+      const unsigned off = (unsigned)(hi * RB) + ((((unsigned)(p ^ hi)) << 4) ^ (32u * (unsigned)(c & 7)));
+      load_lds16_saddr(page_base + 2 * c * RB, off, nope + c * 1024);
+    }
+    if constexpr (ROPE > 0) {
+      const unsigned off = (unsigned)(r8 * RB + kNope) + ((((unsigned)(p8 ^ (r8 >> 1))) << 4) ^ (64u * (unsigned)(e & 1)));
+      load_lds16_saddr(page_base + 8 * e * RB, off, rope + e * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * e + i;
+      const int row = 2 * c + hi;
+      if (row < valid)
+        load_lds16(page_base + (unsigned)(row * RB + ((p ^ (row & 15)) << 4)), nope + c * 1024);
+      else
+        lds_zero16(nope + c * 1024 + lane * 16);
+    }
+    if constexpr (ROPE > 0) {
+      const int row = 8 * e + r8;
+      if (row < valid)
+        load_lds16(page_base + (unsigned)(row * RB + kNope + ((p8 ^ ((row >> 1) & 7)) << 4)), rope + e * 1024);
+      else
+        lds_zero16(rope + e * 1024 + lane * 16);
+    }
+    wait_vmcnt<0>();
+  }
+}
+
+template <int ROPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(3, 3)))
+void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
+  constexpr int D = kNope + ROPE;   // q row length
+  constexpr long RB = kNope + 2 * ROPE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + WsX::bytes];
+  uint8_t* const lds = lds_;
+  uint8_t* const xp = lds + Tile<ROPE>::lds_bytes;
+  float* const xalpha = reinterpret_cast<float*>(xp + 2 * WsX::p_bytes);
+  int* const xflag = reinterpret_cast<int*>(xp + WsX::flag_off);
+  float* const xfin = reinterpret_cast<float*>(xp + WsX::fin_off);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 31, h = lane >> 5;
+
+  int bid = xcd_grouped_block(blockIdx.x, gridDim.x);
+  const int rg = bid % a.row_groups;
+  bid /= a.row_groups;
+  const int s = bid % a.splits;
+  const int g = bid / a.splits;
+
+  int sk = seq_lens[g];
+  sk = max(0, min(sk, a.max_pages * kKeys));
+  const int units = (sk + kKeys - 1) / kKeys;
+  const int u0 = (int)((long)s * units / a.splits);
+  const int u1 = (int)((long)(s + 1) * units / a.splits);
+  const int ntiles = u1 - u0;
+  const int32_t* bt_row = block_table + (long)g * a.max_pages;
+  auto page_of_lane = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
+
+  if (wave < kSWaves) {
+    // ======================= S-wave: S^T, softmax, P^T ========================
+    const int rb = rg * kSWaves + wave;
+    const bool wave_active = rb < a.row_blocks;
+    const int row = rb * 32 + n;
+    const bool row_ok = row < a.rows;
+    const long qrow_idx = (long)g * a.rows + row;
+    const bool q_ok = row_ok && wave_active;
+    const uint16_t* qsrc = q_ok ? q + qrow_idx * D : q;   // rows outside the problem read row 0, zeroed below
+
+    // Query row n: two passes over its 512 nope values (a 128-register copy
+    // of the raw row next to its codes would not fit three waves per SIMD):
+    // the row max, then the codes, from a second read of the same bytes
+    // (through a pointer the compiler cannot equate with the first, so that
+    // it does not keep the first read's registers alive instead).
+    i32x4 qr_raw[ROPE > 0 ? 4 : 1];
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qr_raw[t] = *reinterpret_cast<const i32x4*>(qsrc + kNope + 16 * t + 8 * h);
+    }
+    int pages_v = page_of_lane(u0 + lane);
+    // (each pass in groups of two fragments, 32 registers of loads in flight:
+    // issued all at once the loads alone would need 128)
+    float amax = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(qsrc + 64 * t + 32 * h + 8 * k);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo((unsigned)v[d])), fabsf(bf16_hi((unsigned)v[d]))));
+      }
+      if (t & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    amax = pair_max_swap(amax);
+    const int qe = q_exponent(amax);
+    const int ne = -qe;   // x * 2^-e by exponent adjustment (finite for every bf16 row)
+    const uint16_t* qsrc2 = qsrc;
+    asm volatile("" : "+v"(qsrc2));
+    i32x8 qn[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(qsrc2 + 64 * t + 32 * h + 8 * k);
+        const unsigned w0 = (unsigned)v[0], w1 = (unsigned)v[1], w2 = (unsigned)v[2], w3 = (unsigned)v[3];
+        const int c0 = f32x4_to_fp8x4(ldexpf(bf16_lo(w0), ne), ldexpf(bf16_hi(w0), ne), ldexpf(bf16_lo(w1), ne),
+                                      ldexpf(bf16_hi(w1), ne));
+        const int c1 = f32x4_to_fp8x4(ldexpf(bf16_lo(w2), ne), ldexpf(bf16_hi(w2), ne), ldexpf(bf16_lo(w3), ne),
+                                      ldexpf(bf16_hi(w3), ne));
+        qn[t][2 * k] = q_ok ? c0 : 0;
+        qn[t][2 * k + 1] = q_ok ? c1 : 0;
+        if ((t & 1) && k == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    const float qk_scale = ldexpf(*k_scale, qe);   // q_scale * k_scale on the nope products
+    bf16x8 qr[ROPE > 0 ? 4 : 1];
+    if constexpr (ROPE > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        i32x4 v = qr_raw[t];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] = q_ok ? v[d] : 0;
+        qr[t] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    const int i_tok = row / a.h_q;
+    const int row_len = row_ok ? (a.causal ? sk - (a.s_q - 1 - i_tok) : sk) : 0;   // keys this row may see
+    wait_vmcnt<0>();
+    asm volatile("" : "+v"(pages_v));
+
+    // z (log2 units) = acc * zscale: with rope the nope sums are scaled by
+    // q_scale * k_scale in place before the rope products accumulate onto them
+    // (kept >= 1e-37: a row whose q_scale * k_scale underflows to 0 would turn
+    // masked keys' -inf * 0 into NaN; its logits are ~0 either way)
+    const float zscale = ROPE > 0 ? a.sm_log2 : fmaxf(qk_scale * a.sm_log2, 1e-37f);
+    float m_run = -INFINITY;   // max used for the exponentials (log2 domain)
+    float l_run = 0.f;         // this lane's share of the running sum
+
+    int buf = 0;
+    for (int k = 0; k <= ntiles; ++k) {
+      __syncthreads();   // tile k landed; P^T of tile k-2's parity is free again
+      if (k == ntiles) break;
+      const int par = k & 1;
+      if (k > 0 && (k & 63) == 0) {   // next 64 page ids
+        pages_v = page_of_lane(u0 + k + lane);
+        wait_vmcnt<0>();
+      }
+      const int page_cur = __builtin_amdgcn_readlane(pages_v, k & 63);
+      const uint8_t* nope = lds + buf * kNopeRegion;
+      const uint8_t* rope = lds + kRopeBase + buf * kRopeRegion;
+      const int unit = u0 + k;
+
+      // ---- S^T = K Q^T (fragment ring of PD items, alternating key blocks) ----
+      __builtin_amdgcn_s_setprio(3);
+      f32x16 acc[2];
+      {
+        // The lane's fragment addresses (LdsBases' k8 and rp) differ only in
+        // the chunk bits the swizzle XORs: fp8 fragment t, half e is
+        // kbase ^ 16 (4 (t & 3) + e) plus an immediate, rope fragment t is
+        // rbase ^ 32 t. Two bases, recomputed per tile from a lane id the
+        // compiler cannot hoist, and one XOR per address: twelve kept bases
+        // would not fit three waves per SIMD.
+        int lv;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lv));
+        const int krow = key_of_row(lv & 31), hh = lv >> 5;
+        const int kbase = krow * kNope + (((2 * hh) ^ (krow & 15)) << 4);
+        const int rbase = krow * 128 + ((hh ^ ((krow >> 1) & 7)) << 4);
+        constexpr int NN = 16, NI = NN + (ROPE > 0 ? 8 : 0), PD = 3;
+        i32x4 rl[PD], rh[PD];
+        auto load = [&](int f) {
+          const int slot = f % PD, kb = f & 1;
+          if (f < NN) {
+            const int t = f >> 1;
+            const int c = 32 * kb * kNope + 256 * (t >> 2);
+            rl[slot] = lds_ld16(nope, (kbase ^ (16 * (4 * (t & 3)))) + c);
+            rh[slot] = lds_ld16(nope, (kbase ^ (16 * (4 * (t & 3) + 1))) + c);
+          } else {
+            rl[slot] = lds_ld16(rope, (rbase ^ (32 * ((f - NN) >> 1))) + 32 * kb * 128);
+          }
+        };
+#pragma unroll
+        for (int f = 0; f < PD; ++f) load(f);
+#pragma unroll
+        for (int f = 0; f < NI; ++f) {
+          const int slot = f % PD, kb = f & 1;
+          const i32x4 lo = rl[slot], hi = rh[slot];
+          if (f + PD < NI) load(f + PD);
+          if (f < NN) {
+            const i32x8 kf = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if (f < 2) mfma_fp8_32x32x64_first(acc[kb], kf, qn[f >> 1]);
+            else mfma_fp8_32x32x64(acc[kb], kf, qn[f >> 1]);
+            if constexpr (ROPE > 0) {
+              if (f == NN - 1) {
+                // nope sums complete: scale them, then add the rope products
+                s_nop_result2(acc[0], acc[1]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  acc[0][r] *= qk_scale;
+                  acc[1][r] *= qk_scale;
+                }
+              }
+            }
+          } else {
+            const bf16x8 kr = __builtin_bit_cast(bf16x8, lo);
+            if (f < NN + 2) mfma_bf16_32x32x16_after_valu(acc[kb], kr, qr[(f - NN) >> 1]);
+            else mfma_bf16_32x32x16(acc[kb], kr, qr[(f - NN) >> 1]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      s_nop_result2(acc[0], acc[1]);
+      __builtin_amdgcn_s_setprio(0);
+
+      // ---- mask + online softmax (log2 domain), P^T to LDS ----------------------
+      const bool page_ok = page_valid(page_cur);
+      const bool full = page_ok && (unit + 1) * kKeys <= sk - (a.causal ? a.s_q - 1 : 0);
+      const int limit = page_ok ? row_len - unit * kKeys : 0;
+      if (!full) {
+        // register r of key block kb is key 32 kb + 8 j + 4 ((j + h) & 1) + r % 4
+        // (j = r / 4): compile-time offsets against two per-lane limits, so
+        // that no per-lane key index is kept across the tile loop
+        const int lim_e = limit - 4 * h, lim_o = limit - 4 * (1 - h);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = r >> 2;
+            const int kc = 32 * kb + 8 * j + (r & 3);
+            acc[kb][r] = kc < ((j & 1) ? lim_o : lim_e) ? acc[kb][r] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
+      mx = pair_max_swap(mx) * zscale;
+
+      const bool raise = mx > m_run + Soft<DOT_FP8>::tau;
+      bool flagged = false;
+      if (__ballot(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+        l_run *= alpha;
+        // O needs rescaling only where a finite max was raised
+        flagged = __ballot(raise && m_run != -INFINITY) != 0ull;
+        if (flagged && h == 0) xalpha[par * (kSWaves * 32) + wave * 32 + n] = alpha;
+        m_run = m_new;
+      }
+      const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT_FP8>::ps_log2;
+      float psum = 0.f;
+      i32x8 pb;
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const int kb = q4 >> 2, r0 = 4 * (q4 & 3);
+        float pe[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pe[r] = __builtin_amdgcn_exp2f(fmaf(acc[kb][r0 + r], zscale, -m_exp));
+          psum += pe[r];
+        }
+        pb[q4] = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
+      }
+      l_run += psum;
+      uint8_t* pdst = xp + par * WsX::p_bytes + wave * 2048 + lane * 16;
+      *reinterpret_cast<i32x4*>(pdst) = i32x4{pb[0], pb[1], pb[2], pb[3]};
+      *reinterpret_cast<i32x4*>(pdst + 1024) = i32x4{pb[4], pb[5], pb[6], pb[7]};
+      if (lane == 0) xflag[4 * par + wave] = flagged ? 1 : 0;
+      buf = buf == kBufs - 1 ? 0 : buf + 1;
+    }
+
+    // ---- epilogue: per-row output scale for the PV-waves; lse ---------------------
+    const float l_tot = pair_sum_swap(l_run);
+    const bool nonempty = l_tot > 0.f;
+    // splits == 1: v_scale / l; else the partials' 1 / l (fp16 partials,
+    // |value| <= 448; the combine applies v_scale)
+    if (h == 0) xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? *v_scale : 1.f) / l_tot : 0.f;
+    if (wave_active && h == 0) {
+      const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT_FP8>::ps_log2 : -INFINITY;
+      if (a.splits == 1) {
+        if (row_ok) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
+      } else {
+        part_lse[(((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n] = lse2;
+      }
+    }
+    __syncthreads();
+  } else {
+    // ===================== PV-wave: tile copies, O^T += V^T P^T =====================
+    const int e = wave - kSWaves;          // dv slice 64e .. 64e + 63 (blocks 2e, 2e + 1)
+    int pages_v = page_of_lane(u0 + lane);
+    wait_vmcnt<0>();
+    asm volatile("" : "+v"(pages_v));
+    auto issue = [&](int t, int bufi) {
+      const int page = __builtin_amdgcn_readlane(pages_v, t & 63);
+      const bool ok = page_valid(page);
+      const int valid = ok ? min(kKeys, sk - (u0 + t) * kKeys) : 0;
+      ws_issue_tile<ROPE>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, e);
+    };
+    if (ntiles > 0) issue(0, 0);
+
+    // V^T lane bases of the two dv blocks (2e, 2e + 1)
+    const int vt0 = vt_lane_base(lane, (2 * e) & 7), vt1 = vt_lane_base(lane, (2 * e + 1) & 7);
+    const int vhi = 256 * ((2 * e) >> 3);   // dv blocks 8..15: the upper half of each nope row
+
+    // O^T accumulators: O[j][r] = dv block 2e + j of row block r (VGPRs)
+    f32x16 O[2][kSWaves];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < kSWaves; ++r) O[j][r] = f32x16{};
+
+    int bufp = 2;   // ring buffer of tile k-1
+    for (int k = 0; k <= ntiles; ++k) {
+      wait_vmcnt<0>();   // this wave's copies of tile k have landed
+      __syncthreads();
+      const int buf_next = bufp == 0 ? 2 : bufp - 1;   // (k + 1) % 3
+      if (k + 1 < ntiles) {
+        if (((k + 1) & 63) == 0) {   // next 64 page ids
+          pages_v = page_of_lane(u0 + k + 1 + lane);
+          wait_vmcnt<0>();
+        }
+        issue(k + 1, buf_next);
+      }
+      if (k > 0) {
+        const int pp = (k - 1) & 1;
+        const i32x4 fl = *reinterpret_cast<const i32x4*>(xflag + 4 * pp);
+        const uint8_t* vnope = lds + bufp * kNopeRegion;
+        const uint8_t* pprev = xp + pp * WsX::p_bytes;
+        i32x8 vr[2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i32x2 v0 = lds_tr8(vnope, vt0 + 8192 * u + vhi);
+          const i32x2 v1 = lds_tr8(vnope, vt1 + 8192 * u + vhi);
+          vr[0][2 * u] = v0.x;
+          vr[0][2 * u + 1] = v0.y;
+          vr[1][2 * u] = v1.x;
+          vr[1][2 * u + 1] = v1.y;
+        }
+        // rescale O for the rows whose max tile k-1 raised (rare), before its products
+        if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+          asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+          const float* al = xalpha + pp * (kSWaves * 32);
+#pragma unroll
+          for (int r = 0; r < kSWaves; ++r) {
+            if (__builtin_amdgcn_readfirstlane(fl[r])) {
+              const float f = al[r * 32 + n];
+#pragma unroll
+              for (int x = 0; x < 16; ++x) {
+                O[0][r][x] *= f;
+                O[1][r][x] *= f;
+              }
+            }
+          }
+          asm volatile("s_nop 4" ::: "memory");
+        }
+#pragma unroll
+        for (int r = 0; r < kSWaves; ++r) {
+          const i32x4 lo = lds_ld16(pprev, r * 2048 + lane * 16);
+          const i32x4 hi = lds_ld16(pprev, r * 2048 + 1024 + lane * 16);
+          const i32x8 pt = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          mfma_fp8_32x32x64(O[0][r], vr[0], pt);
+          mfma_fp8_32x32x64(O[1][r], vr[1], pt);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      bufp = bufp == kBufs - 1 ? 0 : bufp + 1;
+    }
+
+    // ---- epilogue ----------------------------------------------------------------------
+    __syncthreads();   // the S-waves' per-row scales are in LDS
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last P.V MFMAs done
+    // O^T register x of block (j, r): dv 32 (2e + j) + 8 (x / 4) + 4 h + x % 4, row 32 rbr + n
+#pragma unroll
+    for (int r = 0; r < kSWaves; ++r) {
+      const int rbr = rg * kSWaves + r;
+      if (rbr >= a.row_blocks) break;
+      const float inv = xfin[r * 32 + n];
+      const int rowr = rbr * 32 + n;
+      if (a.splits == 1) {
+        if (rowr < a.rows) {
+          uint16_t* orow = out + ((long)g * a.rows + rowr) * kNope;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int dv = 32 * (2 * e + j) + 8 * e4 + 4 * h;
+              const f32x16& o = O[j][r];
+              uint2 w;
+              w.x = bf16x2_bits(o[4 * e4] * inv, o[4 * e4 + 1] * inv);
+              w.y = bf16x2_bits(o[4 * e4 + 2] * inv, o[4 * e4 + 3] * inv);
+              *reinterpret_cast<uint2*>(orow + dv) = w;
+            }
+        }
+      } else {
+        // partials in the accumulator's own register layout, as the combine reads them
+        const long frag = ((long)s * a.groups + g) * a.row_blocks + rbr;
+        uint16_t* po = part_o + frag * (16 * 64 * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const f32x16& o = O[j][r];
+          i32x4* dst = reinterpret_cast<i32x4*>(po + ((2 * e + j) * 64 + lane) * 16);
+#pragma unroll
+          for (int e8 = 0; e8 < 2; ++e8) {
+            i32x4 w;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) w[d] = (int)half2_bits(o[8 * e8 + 2 * d] * inv, o[8 * e8 + 2 * d + 1] * inv);
+            dst[e8] = w;
+          }
+        }
+      }
+    }
+  }
+}
+
+bool decode_ws_eligible(const DecodeLaunch& d) {
+  return d.dot == DOT_FP8 && !d.per_token && !d.fnuz && d.topk == 0 && d.row_blocks >= 3 && !d.rows_kernel &&
+         !d.dv_split_kernel && !d.gather_v;
+}
+
+hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
+#define MLA_WS_ARGS d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
+  if (d.d_rope == 64)
+    hipLaunchKernelGGL((mla_decode_ws_kernel<64>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+  else
+    hipLaunchKernelGGL((mla_decode_ws_kernel<0>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+#undef MLA_WS_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -129,17 +129,28 @@ typedef struct mla_params {
  * failing check's code. */
 MLA_API int32_t mla_fp8_validate(const mla_params* p);
 
-/* Split count the decode will use. num_splits > 0 is taken as given (capped
- * at MLA_MAX_SPLITS); 0 selects the smallest s with groups * s >= cu_count,
+/* Split count the decode will use. The split-KV scheme is InfiniCore PR #1568's
+ * split-kv commit: the token range of a sequence is sharded over several
+ * workgroups, the split count comes from an automatic occupancy ("waves")
+ * heuristic that leaves an already large grid unsplit, and an environment
+ * variable overrides it. Here: num_splits > 0 is taken as given (capped at
+ * MLA_MAX_SPLITS); 0 selects the smallest s with groups * s >= cu_count,
  * capped at 16 and at the number of 64-key units per sequence, where groups is
  * batch (dense) or batch * s_q (sparse). The environment variable
  * MLA_FP8_NUM_SPLITS, when set to a positive integer, replaces the automatic
- * choice. Returns a value >= 1, or a negative status on invalid *p. Host-only. */
+ * choice. Returns a value >= 1, or a negative status on invalid *p. Host-only,
+ * no HIP call. */
 MLA_API int32_t mla_fp8_decode_resolve_splits(const mla_params* p, int32_t num_splits,
                                               int32_t cu_count);
 
 /* Workspace bytes needed for a resolved split count (0 when splits == 1).
- * Returns 0 for invalid *p or splits < 1. Host-only. */
+ * As in InfiniCore PR #1568's split-kv commit, where the decode's workspace
+ * grows from zero to splits x sequences x heads x (value size + 2) floats,
+ * the workspace holds one partial per split and query row: here the 512
+ * partial output values in fp16 and one f32 log-sum-exp, padded to 32-row
+ * blocks: splits * groups * ceil(rows / 32) * (32 KiB + 128 B). The caller
+ * owns it; its contents need no initialization and are overwritten by every
+ * call. Returns 0 for invalid *p or splits < 1. Host-only, no HIP call. */
 MLA_API size_t mla_fp8_decode_workspace_size(const mla_params* p, int32_t splits);
 
 /* The decode. Enqueues one kernel (splits == 1) or the split kernel and the
@@ -198,10 +209,36 @@ MLA_API int32_t mla_fp8_quantize_kv(int32_t num_tokens, int32_t d_rope, int32_t 
                                     float* k_scale, float* v_scale, int32_t compute_scale, void* workspace,
                                     size_t workspace_bytes, void* hip_stream);
 
-/* Static description of a status code. Never NULL. */
+/* Static description of a status code. Never NULL. The codes follow the
+ * pages' failure conventions: an F8 cache without its scales fails loudly as
+ * a bad parameter rather than being read unscaled (InfiniCore PR #1568, the
+ * commit that makes a scale-less F8 cache fail with Bad Parameter), and a
+ * configuration the library does not implement is refused with its own code
+ * rather than misread (InfiniCore PR #1568, the backends commit returning
+ * NOT_IMPLEMENTED for F8 caches; ROCm/aiter PR #6199, the foreign-encoding
+ * refusal). */
 MLA_API const char* mla_fp8_status_string(int32_t status);
 
 /* --- test and measurement exports (device pointers, caller's stream) --- */
+
+/* The decode (arguments as for mla_fp8_decode) with an internal kernel
+ * variant forced, so that tests can compare the variants on the same inputs:
+ *   MLA_VARIANT_GATHER_V    V^T operands by byte gathers instead of the
+ *                           transposing LDS reads
+ *   MLA_VARIANT_ROWS        fp8 dots: the row-block kernel (P.V split by row
+ *                           block) instead of the default
+ *   MLA_VARIANT_DV_SPLIT    fp8 dots: the four-wave dv-split kernel instead of
+ *                           the default
+ * 0 is the production choice. Unknown bits are MLA_ERR_SHAPE. */
+#define MLA_VARIANT_GATHER_V 1
+#define MLA_VARIANT_ROWS 2
+#define MLA_VARIANT_DV_SPLIT 4
+MLA_API int32_t mla_fp8_debug_decode_variant(const mla_params* p, const void* q, const void* kv_cache,
+                                             const int32_t* block_table, const int32_t* seq_lens,
+                                             const float* k_scale, const float* v_scale,
+                                             int32_t num_splits, void* out, float* lse,
+                                             const int32_t* indices, void* workspace,
+                                             size_t workspace_bytes, int32_t variant, void* hip_stream);
 
 /* Decodes n e4m3fn bytes with the same device routines the decode kernels
  * use: to f32 (out_f32, may be NULL) and to bf16 bits (out_bf16, may be NULL). */

@@ -177,12 +177,13 @@ def split_ranges(n_units, num_splits):
 def split_partials(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale,
                    num_splits, *, d_nope=512, d_rope=64, causal=True,
                    softmax_scale=None, indices=None, q_nope_override=None,
-                   page_block=64):
+                   page_block=64, encoding="e4m3fn"):
     """Split-KV partials: per split s, (o_s, lse_s) over that split's keys.
 
     Dense: the sequence's pages are cut into ``num_splits`` contiguous,
     page-aligned ranges. Sparse: the index list is cut the same way in units
     of 64 entries. A split with no visible key for a row gives (0, -inf).
+    ``encoding`` names the cache's one-byte code, as for mla_decode.
     Returns o [S, b, s_q, h_q, d_nope], lse [S, b, s_q, h_q].
     """
     q = query_f64(q_bits, q_nope_override, d_nope)
@@ -201,7 +202,7 @@ def split_partials(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale,
                     rows = _positions_to_rows(kv_cache, block_table[b], pos, page_block)
                     k, v = dequant_keys_values(rows, scale_at(k_scale, block_table[b], pos, page_block),
                                                scale_at(v_scale, block_table[b], pos, page_block),
-                                               d_nope, d_rope)
+                                               d_nope, d_rope, encoding)
                     o[s, b, i], lse[s, b, i] = _attend(q[b, i], k, v, scale)
             else:
                 entries = np.asarray(indices[b, i]).astype(np.int64)
@@ -212,7 +213,7 @@ def split_partials(q_bits, kv_cache, block_table, seq_lens, k_scale, v_scale,
                     rows = _positions_to_rows(kv_cache, block_table[b], pos, page_block)
                     k, v = dequant_keys_values(rows, scale_at(k_scale, block_table[b], pos, page_block),
                                                scale_at(v_scale, block_table[b], pos, page_block),
-                                               d_nope, d_rope)
+                                               d_nope, d_rope, encoding)
                     o[s, b, i], lse[s, b, i] = _attend(q[b, i], k, v, scale)
     return o, lse
 
@@ -258,6 +259,12 @@ def quantize_q_rows(q_nope):
 
 
 def dequantized_q_nope(q_bits, d_nope=512):
-    """Q' (the fp8-dot path's query, dequantized) as float64 [..., d_nope]."""
+    """Q' (the fp8-dot path's query, dequantized) as float64 [..., d_nope].
+
+    Each row's nope part is quantized as quantize_q_rows does (the query
+    quantized in-kernel to the fp8 range, ROCm/aiter PR #6199, Technical
+    details) and mapped back: Q' = decode(code) * 2**e, so that |Q' - q| is at
+    most half an e4m3fn step at q's magnitude times 2**e.
+    """
     codes, exps = quantize_q_rows(bf16_bits_to_f64(q_bits)[..., :d_nope])
     return decode_e4m3fn(codes) * np.ldexp(1.0, exps.astype(np.int64))[..., None]

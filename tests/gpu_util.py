@@ -7,7 +7,20 @@ least one key; `lse` within 1e-3 absolute on those rows; rows with no visible
 key must give out == 0 exactly and lse == -inf. For fp8 dots the lse is
 compared with the oracle evaluated at the kernel's quantized query Q' (the
 quantization itself is checked bit-exactly elsewhere), and `out` with the
-oracle at the exact bf16 query.
+oracle at the exact bf16 query. The lse difference from the oracle at the
+exact bf16 query is reported beside it (for fp8 dots it is the effect of
+quantizing Q and exceeds 1e-3 on short or peaky rows).
+
+Beside the whole-tensor figure every query row (b, i, h) is held to its own
+relative L2 error against the oracle at the query the kernel multiplies (Q'
+for fp8 dots, whose effect on a row the oracle reproduces exactly, and the
+bf16 query for bf16 dots). What is left is the rounding of P and of the
+output: fp8 dots round each weight to e4m3fn (3 mantissa bits: at most 2^-4
+relative while normal, about 3.6% RMS), and these errors are independent
+across keys and averaged over the 512 output dims, so a row's error sits near
+that RMS; the bound is 2^-3 = 12.5%. bf16 dots round P and the output to bf16
+(2^-9 each, about 0.16% RMS together); the bound is 1%. A zeroed, stale or
+misplaced row block gives a row error near 100%.
 """
 
 import functools
@@ -19,6 +32,7 @@ import fp8_kv_cache_paged_amd as mla
 from oracle import attn
 
 OUT_TOL = {"bf16": 5e-3, "fp8": 5e-2}
+ROW_TOL = {"bf16": 1e-2, "fp8": 0.125}
 LSE_TOL = 1e-3
 
 
@@ -68,9 +82,13 @@ class OracleCache:
         return oracle(self.w, q_prime=True)
 
 
-def compare(out, lse, ref_out, ref_lse, ref_lse_for_lse=None, dot="fp8"):
-    """Returns a dict of error figures and asserts the tolerances."""
+def compare(out, lse, ref_out, ref_lse, ref_lse_for_lse=None, dot="fp8", ref_out_rows=None):
+    """Returns a dict of error figures and asserts the tolerances. ref_out,
+    ref_lse: the oracle at the bf16 query; ref_lse_for_lse and ref_out_rows:
+    the oracle at the query the kernel multiplies (Q' for fp8 dots), used for
+    the lse and per-row checks (default: ref_lse, ref_out)."""
     ref_lse_l = ref_lse if ref_lse_for_lse is None else ref_lse_for_lse
+    ref_rows = ref_out if ref_out_rows is None else ref_out_rows
     empty = np.isneginf(ref_lse)
     assert np.array_equal(np.isneginf(lse), empty), "rows with no visible key must give lse = -inf (and only they)"
     assert np.all(out[empty] == 0), "rows with no visible key must give out = 0"
@@ -80,8 +98,14 @@ def compare(out, lse, ref_out, ref_lse, ref_lse_for_lse=None, dot="fp8"):
     den = np.linalg.norm(ref_out[live])
     rel = float(num / den) if den > 0 else float(num)
     dl = float(np.max(np.abs(lse[live] - ref_lse_l[live]))) if live.any() else 0.0
-    res = {"rel_l2": rel, "lse_max_abs": dl}
+    dl_plain = float(np.max(np.abs(lse[live] - ref_lse[live]))) if live.any() else 0.0
+    row_err = np.linalg.norm((out - ref_rows)[live], axis=-1)
+    row_ref = np.linalg.norm(ref_rows[live], axis=-1)
+    row_rel = row_err / np.where(row_ref > 0, row_ref, 1.0)
+    row_max = float(row_rel.max()) if row_rel.size else 0.0
+    res = {"rel_l2": rel, "row_rel_l2_max": row_max, "lse_max_abs": dl, "lse_max_abs_vs_bf16q": dl_plain}
     assert rel <= OUT_TOL[dot], f"rel-L2 {rel:.3e} > {OUT_TOL[dot]} ({dot} dots)"
+    assert row_max <= ROW_TOL[dot], f"worst row rel-L2 {row_max:.3e} > {ROW_TOL[dot]} ({dot} dots)"
     assert dl <= LSE_TOL, f"max |dlse| {dl:.3e} > {LSE_TOL}"
     return res
 
@@ -90,5 +114,5 @@ def check(w, oc, dot, num_splits=None, t=None, **kw):
     t = device_inputs(w) if t is None else t
     out, lse = run(w, t, dot, num_splits, **kw)
     ref_o, ref_l = oc.exact
-    lse_ref = oc.qprime[1] if dot == "fp8" else ref_l
-    return compare(out, lse, ref_o, ref_l, lse_ref, dot)
+    ref_q = oc.qprime if dot == "fp8" else oc.exact
+    return compare(out, lse, ref_o, ref_l, ref_q[1], dot, ref_out_rows=ref_q[0])

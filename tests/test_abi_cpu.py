@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
     assert set(names) <= exported
@@ -153,6 +153,18 @@ def test_decode_rejects_before_any_launch(L):
     st = L.mla_fp8_decode(ctypes.byref(p), *[ctypes.c_void_p(16)] * 6, 2, ctypes.c_void_p(16),
                           ctypes.c_void_p(16), None, None, 0, None)
     assert st == mla.MLA_ERR_WORKSPACE
+
+
+def test_decode_variant_rejects_unknown_bits_before_any_launch(L):
+    p = good()
+    args = [ctypes.byref(p)] + [ctypes.c_void_p(16)] * 6 + [1, ctypes.c_void_p(16), ctypes.c_void_p(16), None,
+                                                             None, 0]
+    assert L.mla_fp8_debug_decode_variant(*args, 8, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_fp8_debug_decode_variant(*args, -1, None) == mla.MLA_ERR_SHAPE
+    # known bits pass the variant check and fail later on the invalid params
+    bad = good(h_kv=2)
+    args[0] = ctypes.byref(bad)
+    assert L.mla_fp8_debug_decode_variant(*args, mla.MLA_VARIANT_ROWS, None) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_debug_exports_check_arguments(L):

@@ -44,11 +44,18 @@ def test_query_quantization_matches_oracle(shape):
     flat[-1, :512] = fp8.f32_to_bf16_bits(np.float32(1e-30))   # a tiny row (large 2^-e)
     if flat.shape[0] > 2:
         flat[1, :512] = fp8.f32_to_bf16_bits(np.float32(448.0))
+    if flat.shape[0] > 4:
+        # amax 1e-37: 2^-e lies beyond float32's range; bf16 subnormals
+        flat[2, :512] = fp8.f32_to_bf16_bits(np.linspace(-1e-37, 1e-37, 512, dtype=np.float32))
+        flat[3, :512] = np.arange(512, dtype=np.uint16) % 0x7F + 1
     q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(DEV)
     codes, exps = mla.debug_quantize_q(q)
     ref_codes, ref_exps = attn.quantize_q_rows(fp8.bf16_bits_to_f64(qb)[..., :512])
     assert np.array_equal(exps.cpu().numpy(), ref_exps)
     assert np.array_equal(codes.cpu().numpy(), ref_codes)
+    # the decode on the same rows stays finite (the tiny rows give uniform weights)
+    if flat.shape[0] > 4:
+        assert np.all(np.abs(ref_exps.reshape(-1)[2:4]) > 127)
 
 
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("mtp", {"batch": 3, "seq_len": [8196, 65, 0]}),

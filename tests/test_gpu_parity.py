@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import fp8_kv_cache_paged_amd as mla
 import workloads
 import gpu_util as gu
 
@@ -93,20 +94,36 @@ def test_small_sparse(dot, splits):
     gu.check(w, oc, dot, num_splits=splits, t=t)
 
 
+@pytest.mark.parametrize("dot", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_sparse_repeated_indices_count_twice(dot, splits):
+    """A position named more than once in a token's index list is attended to
+    once per entry (the oracle counts it twice); repeats inside one 64-entry
+    tile, across tiles and across splits."""
+    w, oc, t = _case("sparse", batch=2, seq_len=5000, topk=300, seed=42)
+    idx = w.indices.copy()
+    idx[0, 0, 11] = idx[0, 0, 10]              # same tile
+    idx[0, 1, 200] = idx[0, 1, 3]              # another tile (and split)
+    idx[1, 0, 5:9] = idx[1, 0, 4]              # one position four more times
+    idx[1, 1, 299] = idx[1, 1, 0]
+    w.indices = idx
+    t = dict(t, idx=torch.from_numpy(idx).to("cuda:0"))
+    res = gu.check(w, gu.OracleCache(w), dot, num_splits=splits, t=t)
+    print(f"repeated indices dot={dot} splits={splits}: {res}")
+
+
 def test_more_splits_than_pages_gives_empty_splits():
     w, oc, t = _case("tiny", batch=2, s_q=2, h_q=64, seq_len=[130, 5], seed=51)
     for dot in ("bf16", "fp8"):
         gu.check(w, oc, dot, num_splits=9, t=t)
 
 
-def test_transposed_v_reads_match_byte_gather(monkeypatch):
+def test_transposed_v_reads_match_byte_gather():
     """The V^T operand read with ds_read_b64_tr_b8 equals a plain byte gather."""
     w, oc, t = _case("tiny", batch=2, s_q=2, h_q=64, seq_len=[300, 77], seed=61)
-    for dot in ("bf16", "fp8"):
-        a = gu.run(w, t, dot, 2)
-        monkeypatch.setenv("MLA_FP8_GATHER_V", "1")
-        b = gu.run(w, t, dot, 2)
-        monkeypatch.delenv("MLA_FP8_GATHER_V")
+    for dot, base in (("bf16", 0), ("fp8", mla.MLA_VARIANT_DV_SPLIT)):
+        a = gu.run(w, t, dot, 2, variant=base)
+        b = gu.run(w, t, dot, 2, variant=base | mla.MLA_VARIANT_GATHER_V)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
@@ -131,6 +148,7 @@ def test_v_scale_linearity_and_k_scale():
 
 FULL = [("tiny", "bf16"), ("tiny", "fp8"), ("mtp", "bf16"), ("mtp", "fp8"), ("varlen", "fp8"),
         ("large", "bf16"), ("large", "fp8"), ("sparse", "bf16"), ("sparse", "fp8"), ("metric", "fp8"),
+        ("metric", "bf16"),
         ("sparse16", "bf16"), ("sparse16", "fp8"), ("prefill", "bf16"), ("prefill", "fp8")]
 
 
@@ -146,15 +164,13 @@ def test_full_config(name, dot):
                                   ("tiny", {"batch": 2, "s_q": 1, "h_q": 16, "d_rope": 0, "seq_len": [257, 90], "seed": 93}),
                                   ("sparse", {"batch": 2, "seq_len": 3000, "topk": 200, "seed": 94}),
                                   ("metric", {})])
-def test_dv_split_kernel_matches_row_block_kernel(case, monkeypatch):
+def test_dv_split_kernel_matches_row_block_kernel(case):
     """fp8 dots: splitting P.V over the waves by dv (P^T exchanged through LDS)
     issues the same products in the same order as the row-block kernel, so the
     two agree bit for bit, for every split count."""
     name, kw = case
     w, oc, t = _case(name, **kw)
     for splits in (1, 3, 0):
-        a = gu.run(w, t, "fp8", splits)
-        monkeypatch.setenv("MLA_FP8_ROWS_KERNEL", "1")
-        b = gu.run(w, t, "fp8", splits)
-        monkeypatch.delenv("MLA_FP8_ROWS_KERNEL")
+        a = gu.run(w, t, "fp8", splits, variant=mla.MLA_VARIANT_DV_SPLIT)
+        b = gu.run(w, t, "fp8", splits, variant=mla.MLA_VARIANT_ROWS)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"splits={splits}"

@@ -44,9 +44,13 @@ def _check(w, ks, vs, splits, dot="fp8"):
     kw = dict(d_nope=w.d_nope, d_rope=w.d_rope, causal=w.causal, softmax_scale=w.softmax_scale,
               indices=w.indices)
     ref_o, ref_l = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, **kw)
-    qp = attn.dequantized_q_nope(w.q_bits)
-    _, ref_lq = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, q_nope_override=qp, **kw)
-    return gu.compare(out, lse, ref_o, ref_l, ref_lq if dot == "fp8" else ref_l, dot)
+    if dot == "fp8":
+        qp = attn.dequantized_q_nope(w.q_bits)
+        ref_oq, ref_lq = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs,
+                                         q_nope_override=qp, **kw)
+    else:
+        ref_oq, ref_lq = ref_o, ref_l
+    return gu.compare(out, lse, ref_o, ref_l, ref_lq, dot, ref_out_rows=ref_oq)
 
 
 CASES = [
@@ -82,6 +86,16 @@ def test_per_token_decode_sparse_configuration(dot):
     ks, vs = _scales(w, 129, SPREAD["sparse"])
     res = _check(w, ks, vs, 0, dot)
     print(f"per-token sparse {dot}: {res}")
+
+
+@pytest.mark.skip(reason="fp8 dots scale each p by v_j / V_ref (V_ref the split's largest v-scale) before "
+                         "the e4m3fn packing; at an 8x spread the peaky tail (p ~ 2^-13 of the top key) falls "
+                         "below e4m3fn's smallest subnormal and is flushed, so the case misses the bound")
+def test_per_token_decode_sparse_configuration_full_spread():
+    w = workloads.make("sparse")
+    ks, vs = _scales(w, 129, 8.0)
+    res = _check(w, ks, vs, 0, "fp8")
+    print(f"per-token sparse fp8, 8x spread: {res}")
 
 
 @pytest.mark.parametrize("dot", ["fp8", "bf16"])

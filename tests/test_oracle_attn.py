@@ -356,3 +356,60 @@ def test_split_invariance_per_token(num_splits):
     co, cl = attn.combine(po, pl)
     np.testing.assert_allclose(co, o, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(cl, l, rtol=0, atol=1e-12)
+
+
+# ---- Q' (the fp8-dot path's dequantized query) --------------------------------
+
+def _brute_force_q_prime(q_row):
+    """Q' of one row from the definition, with an outside codec: the smallest
+    integer e with amax <= 448 * 2**e (searched upwards), torch's
+    float8_e4m3fn cast of q * 2**-e, torch's decode, times 2**e."""
+    amax = float(np.abs(q_row).max())
+    e = 0
+    if amax > 0:
+        e = -200
+        while amax > 448.0 * 2.0 ** e:
+            e += 1
+    scaled = torch.from_numpy(q_row * 2.0 ** -e)
+    back = scaled.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return back * 2.0 ** e, e
+
+
+def _e4m3fn_half_step(x):
+    """Half the spacing of e4m3fn values around |x| <= 448 (2**-10 in the subnormal range)."""
+    a = np.abs(x)
+    ex = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (ex - 4)
+
+
+def test_dequantized_q_nope_by_brute_force_and_error_bound():
+    """ROCm/aiter PR #6199, Technical details: the query is quantized in-kernel
+    to the fp8 range. Q' must equal the brute-force definition bit for bit and
+    lie within half an e4m3fn step (times the row's 2**e) of q."""
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=8, seq_len=64, seed=5)
+    bits = w.q_bits.copy()
+    flat = bits.reshape(-1, bits.shape[-1])
+    # special rows: all zero; amax 1e-37 (2**-e beyond float32's range); bf16
+    # subnormals; an amax of exactly 448 * 2**3; a row of one large value
+    tiny = np.float32(1e-37)
+    flat[0, :512] = 0
+    flat[1, :512] = (torch.from_numpy(np.linspace(-1, 1, 512, dtype=np.float32) * tiny)
+                     .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    flat[2, :512] = np.arange(512, dtype=np.uint16) % 0x7F + 1          # positive bf16 subnormals
+    flat[3, :512] = (torch.full((512,), 3.0).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    flat[3, 7] = torch.tensor([448.0 * 8]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0]
+    flat[4, :512] = 0
+    flat[4, 100] = torch.tensor([-1.5e5]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0]
+    qp = attn.dequantized_q_nope(bits)
+    q = fp8.bf16_bits_to_f64(bits)[..., :512]
+    qp_f, q_f = qp.reshape(-1, 512), q.reshape(-1, 512)
+    _, exps = attn.quantize_q_rows(q)
+    for r in range(q_f.shape[0]):
+        ref, e = _brute_force_q_prime(q_f[r])
+        np.testing.assert_array_equal(qp_f[r], ref, err_msg=f"row {r}")
+        assert exps.reshape(-1)[r] == e
+        bound = _e4m3fn_half_step(q_f[r] * 2.0 ** -e) * 2.0 ** e
+        assert np.all(np.abs(qp_f[r] - q_f[r]) <= bound), f"row {r}"
+    assert np.all(qp_f[0] == 0)
+    assert np.all(np.isfinite(qp_f)) and np.abs(qp_f[1]).max() > 0
+    assert exps.reshape(-1)[3] == 3 and qp_f[3, 7] == 448.0 * 8
