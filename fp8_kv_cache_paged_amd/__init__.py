@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.mla_fp8_debug_quantize_q.restype = i32
         L.mla_fp8_debug_gather.argtypes = [P, vp, vp, vp, vp, vp]
         L.mla_fp8_debug_gather.restype = i32
+        L.mla_fp8_debug_gather_ws.argtypes = [P, vp, vp, vp, vp, vp]
+        L.mla_fp8_debug_gather_ws.restype = i32
         L.mla_fp8_bench_stream_read.argtypes = [vp, sz, vp, vp]
         L.mla_fp8_bench_stream_read.restype = i32
         L.mla_fp8_bench_mfma.argtypes = [i32, i32, i32, vp, vp]
@@ -247,16 +249,19 @@ def debug_quantize_q(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.
 
 
 def debug_gather(kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
-                 stream=None) -> torch.Tensor:
-    """Dense copy [b, max_pages*64, row_bytes] of the cache rows through the decode's paged gather."""
+                 stream=None, loader: str = "dense") -> torch.Tensor:
+    """Dense copy [b, max_pages*64, row_bytes] of the cache rows through the decode's paged gather
+    (loader "dense": the tile loader of mla_decode.hip's kernels; "ws": the sliced loader of the
+    role-split fp8 kernel)."""
     row_bytes = kv_cache.shape[-1] * kv_cache.element_size()
     d_rope = (row_bytes - 512) // 2
     b, mp = block_table.shape
     p = make_params(batch=b, s_q=1, h_q=1, d_rope=d_rope, num_pages=kv_cache.shape[0], max_pages_per_seq=mp,
                     kv_dtype=kv_cache.dtype)
     dense = torch.empty((b, mp * 64, row_bytes), dtype=torch.uint8, device=kv_cache.device)
-    _check(lib().mla_fp8_debug_gather(ctypes.byref(p), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
-                                      _ptr(dense), _stream(stream)), "mla_fp8_debug_gather")
+    fn = lib().mla_fp8_debug_gather_ws if loader == "ws" else lib().mla_fp8_debug_gather
+    _check(fn(ctypes.byref(p), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(dense), _stream(stream)),
+           "mla_fp8_debug_gather")
     return dense
 
 

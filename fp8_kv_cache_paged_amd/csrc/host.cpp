@@ -315,6 +315,21 @@ MLA_API int32_t mla_fp8_debug_gather(const mla_params* p, const void* kv_cache, 
              : MLA_ERR_HIP;
 }
 
+MLA_API int32_t mla_fp8_debug_gather_ws(const mla_params* p, const void* kv_cache, const int32_t* block_table,
+                                        const int32_t* seq_lens, void* dense_out, void* hip_stream) {
+  const int32_t st = validate(p);
+  if (st != MLA_OK) return st;
+  if (kv_cache == nullptr || block_table == nullptr || seq_lens == nullptr || dense_out == nullptr)
+    return MLA_ERR_NULL;
+  if (!aligned(kv_cache, 16) || !aligned(dense_out, 16)) return MLA_ERR_ALIGN;
+  return mla::launch_debug_gather_ws(static_cast<const uint8_t*>(kv_cache), block_table, seq_lens, p->batch,
+                                     p->max_pages_per_seq, p->num_pages, p->d_rope,
+                                     static_cast<uint8_t*>(dense_out), static_cast<hipStream_t>(hip_stream)) ==
+                 hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 MLA_API int32_t mla_fp8_bench_mfma(int32_t dot, int32_t iters, int32_t blocks, float* sink, void* hip_stream) {
   if (sink == nullptr) return MLA_ERR_NULL;
   if ((dot != MLA_DOT_BF16 && dot != MLA_DOT_FP8) || iters < 1 || blocks < 1) return MLA_ERR_SHAPE;

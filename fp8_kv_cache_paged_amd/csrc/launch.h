@@ -67,6 +67,9 @@ hipError_t launch_debug_gather(const uint8_t* kv, const int32_t* block_table,
                                const int32_t* seq_lens, int32_t batch, int32_t max_pages,
                                int32_t num_pages, int32_t d_rope, uint8_t* dense_out,
                                hipStream_t stream);
+hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t batch, int32_t max_pages, int32_t num_pages, int32_t d_rope,
+                                  uint8_t* dense_out, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_mfma_peak(int dot, int iters, int blocks, float* sink, hipStream_t stream);
 

@@ -21,7 +21,19 @@
 //    issues one eighth of the tile copies (global -> LDS).
 // The PV-waves multiply tile k-1 while the S-waves take tile k; one barrier
 // per tile orders the three-tile LDS ring, the P^T exchange (double-buffered
-// by tile parity) and the rescale flags. S-wave r and PV-waves r, r+4 share
+// by tile parity) and the rescale flags.
+//
+// Tile layout: the 32 KiB of nope bytes of a tile are eight 4 KiB slices,
+// slice e holding bytes 64e..64e+63 (dv 64e..64e+63, also K dims 64e..) of
+// all 64 keys, 64 bytes per key with its four 16-byte chunks XOR-swizzled by
+// (key >> 2) & 3; the 64 rope rows (128 B) follow the layout of
+// mla_decode.hip. Both the 16-lane groups of the S^T fragment reads (16
+// consecutive keys, one chunk) and the 32-lane groups of the transposing V^T
+// reads hit 64 distinct banks. With this layout PV-wave e reads only slice e
+// of tile k-1, so it may refill that slice with tile k+2 as soon as its own
+// reads have returned: every copy has two iterations to land in the same
+// three-tile ring (the rope rows of tile k+2 go to the rope slot S^T(k-1)
+// released). S-wave r and PV-waves r, r+4 share
 // SIMD r (waves are placed on the SIMDs round-robin). During its S^T
 // products an S-wave runs at raised priority, so the P.V products fill the
 // matrix core around them rather than delaying them.
@@ -64,52 +76,56 @@ __device__ inline float pair_sum_swap(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The tile copies of PV-wave e: nope copies 4e..4e+3 (rows 2c, 2c+1 each) and
-// rope copy e (rows 8e..8e+7). Lane l of nope copy c moves the chunk at
-// position l % 32 of row 2c + l / 32, i.e. global chunk (l % 32) ^ (row & 15);
-// lane l of rope copy r the chunk at position l % 8 of row 8r + l / 8, i.e.
-// global chunk (l % 8) ^ ((row >> 1) & 7). A full page is copied with the
-// scalar page base; rows at or past `valid` are zero-filled instead (the
-// page's slack, or the whole tile for a missing page), and the wave then
-// drains its copies so that its zero stores and copies land together.
+// Copies of slice e of a tile into nope slot `bufi`: four 1 KiB copies, copy i
+// covering keys 16i..16i+15; lane l moves position l % 4 of key 16i + l / 4,
+// i.e. its logical chunk (l % 4) ^ ((key >> 2) & 3) = (l % 4) ^ (l / 16),
+// from global byte key * RB + 64e + 16 * chunk. A full page is copied with the
+// scalar page base; keys at or past `valid` are zero-filled instead (the
+// page's slack, or the whole tile for a missing page), after which the wave
+// drains its copies.
 template <int ROPE>
-__device__ __attribute__((always_inline)) inline void ws_issue_tile(uint8_t* lds, int bufi, const uint8_t* page_base,
-                                                                    int valid, int e) {
+__device__ __attribute__((always_inline)) inline void ws_issue_nope_slice(uint8_t* lds, int bufi, const uint8_t* page_base,
+                                                                          int valid, int e) {
   constexpr int RB = kNope + 2 * ROPE;
   int lane;   // volatile: recomputed here rather than kept across the tile loop
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-  const int hi = lane >> 5, p = lane & 31, r8 = lane >> 3, p8 = lane & 7;
-  uint8_t* nope = lds + bufi * kNopeRegion;
-  uint8_t* rope = lds + kRopeBase + bufi * kRopeRegion;
+  uint8_t* dst = lds + bufi * kNopeRegion + e * 4096;
+  const unsigned lane_off = (unsigned)((lane >> 2) * RB + 16 * ((lane & 3) ^ (lane >> 4)));
   if (valid == kKeys) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 4 * e + i;
-      // (2c + hi) & 15 = 2 (c & 7) + hi: the lane part is (p ^ hi) << 4 xor 32 (c & 7)
-      const unsigned off = (unsigned)(hi * RB) + ((((unsigned)(p ^ hi)) << 4) ^ (32u * (unsigned)(c & 7)));
-      load_lds16_saddr(page_base + 2 * c * RB, off, nope + c * 1024);
-    }
-    if constexpr (ROPE > 0) {
-      const unsigned off = (unsigned)(r8 * RB + kNope) + ((((unsigned)(p8 ^ (r8 >> 1))) << 4) ^ (64u * (unsigned)(e & 1)));
-      load_lds16_saddr(page_base + 8 * e * RB, off, rope + e * 1024);
-    }
+    for (int i = 0; i < 4; ++i) load_lds16_saddr(page_base + 16 * i * RB + 64 * e, lane_off, dst + i * 1024);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = 4 * e + i;
-      const int row = 2 * c + hi;
-      if (row < valid)
-        load_lds16(page_base + (unsigned)(row * RB + ((p ^ (row & 15)) << 4)), nope + c * 1024);
+      if (16 * i + (lane >> 2) < valid)
+        load_lds16(page_base + (unsigned)(16 * i * RB + 64 * e) + lane_off, dst + i * 1024);
       else
-        lds_zero16(nope + c * 1024 + lane * 16);
+        lds_zero16(dst + i * 1024 + lane * 16);
     }
-    if constexpr (ROPE > 0) {
-      const int row = 8 * e + r8;
-      if (row < valid)
-        load_lds16(page_base + (unsigned)(row * RB + kNope + ((p8 ^ ((row >> 1) & 7)) << 4)), rope + e * 1024);
-      else
-        lds_zero16(rope + e * 1024 + lane * 16);
-    }
+    wait_vmcnt<0>();
+  }
+}
+
+// Rope rows 8e..8e+7 of a tile into rope slot `bufi` (the layout of
+// mla_decode.hip: lane l moves position l % 8 of row 8e + l / 8, i.e. its
+// chunk (l % 8) ^ ((row >> 1) & 7)); rows at or past `valid` zero-filled.
+template <int ROPE>
+__device__ __attribute__((always_inline)) inline void ws_issue_rope(uint8_t* lds, int bufi, const uint8_t* page_base,
+                                                                    int valid, int e) {
+  constexpr int RB = kNope + 2 * ROPE;
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int r8 = lane >> 3, p8 = lane & 7;
+  uint8_t* rope = lds + kRopeBase + bufi * kRopeRegion + e * 1024;
+  if (valid == kKeys) {
+    const unsigned off = (unsigned)(r8 * RB + kNope) + ((((unsigned)(p8 ^ (r8 >> 1))) << 4) ^ (64u * (unsigned)(e & 1)));
+    load_lds16_saddr(page_base + 8 * e * RB, off, rope);
+  } else {
+    const int row = 8 * e + r8;
+    if (row < valid)
+      load_lds16(page_base + (unsigned)(row * RB + kNope + ((p8 ^ ((row >> 1) & 7)) << 4)), rope);
+    else
+      lds_zero16(rope + lane * 16);
     wait_vmcnt<0>();
   }
 }
@@ -243,26 +259,25 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       __builtin_amdgcn_s_setprio(3);
       f32x16 acc[2];
       {
-        // The lane's fragment addresses (LdsBases' k8 and rp) differ only in
-        // the chunk bits the swizzle XORs: fp8 fragment t, half e is
-        // kbase ^ 16 (4 (t & 3) + e) plus an immediate, rope fragment t is
-        // rbase ^ 32 t. Two bases, recomputed per tile from a lane id the
-        // compiler cannot hoist, and one XOR per address: twelve kept bases
-        // would not fit three waves per SIMD.
+        // The lane's fragment addresses: fp8 fragment t, half e is
+        // (kbase ^ 16 e) + 4096 t + 2048 kb, rope fragment t is rbase ^ 32 t
+        // plus an immediate. Two bases, recomputed per tile from a lane id the
+        // compiler cannot hoist (kept bases would not fit three waves per SIMD).
         int lv;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lv));
         const int krow = key_of_row(lv & 31), hh = lv >> 5;
-        const int kbase = krow * kNope + (((2 * hh) ^ (krow & 15)) << 4);
+        const int kbase = krow * 64 + (((2 * hh) ^ ((krow >> 2) & 3)) << 4);   // slice layout
         const int rbase = krow * 128 + ((hh ^ ((krow >> 1) & 7)) << 4);
         constexpr int NN = 16, NI = NN + (ROPE > 0 ? 8 : 0), PD = 3;
         i32x4 rl[PD], rh[PD];
         auto load = [&](int f) {
           const int slot = f % PD, kb = f & 1;
           if (f < NN) {
+            // step t = slice t; key 32 kb + krow; chunks 2h, 2h + 1
             const int t = f >> 1;
-            const int c = 32 * kb * kNope + 256 * (t >> 2);
-            rl[slot] = lds_ld16(nope, (kbase ^ (16 * (4 * (t & 3)))) + c);
-            rh[slot] = lds_ld16(nope, (kbase ^ (16 * (4 * (t & 3) + 1))) + c);
+            const int c = 4096 * t + 2048 * kb;
+            rl[slot] = lds_ld16(nope, kbase + c);
+            rh[slot] = lds_ld16(nope, (kbase ^ 16) + c);
           } else {
             rl[slot] = lds_ld16(rope, (rbase ^ (32 * ((f - NN) >> 1))) + 32 * kb * 128);
           }
@@ -376,20 +391,38 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   } else {
     // ===================== PV-wave: tile copies, O^T += V^T P^T =====================
     const int e = wave - kSWaves;          // dv slice 64e .. 64e + 63 (blocks 2e, 2e + 1)
+    constexpr int kCopies = 4 + (ROPE > 0 ? 1 : 0);   // this wave's copies of one full tile
     int pages_v = page_of_lane(u0 + lane);
     wait_vmcnt<0>();
     asm volatile("" : "+v"(pages_v));
-    auto issue = [&](int t, int bufi) {
+    // keys of tile t that exist (0 for a missing page), and its first cache byte
+    auto tile_src = [&](int t, int& valid) -> const uint8_t* {
       const int page = __builtin_amdgcn_readlane(pages_v, t & 63);
       const bool ok = page_valid(page);
-      const int valid = ok ? min(kKeys, sk - (u0 + t) * kKeys) : 0;
-      ws_issue_tile<ROPE>(lds, bufi, kv + (long)(ok ? page : 0) * kKeys * RB, valid, e);
+      valid = ok ? min(kKeys, sk - (u0 + t) * kKeys) : 0;
+      return kv + (long)(ok ? page : 0) * kKeys * RB;
     };
-    if (ntiles > 0) issue(0, 0);
+    // tiles 0 and 1 before the loop; then tile k+2 during iteration k
+    bool tile1_full = false;
+    for (int t = 0; t < 2 && t < ntiles; ++t) {
+      int valid;
+      const uint8_t* src = tile_src(t, valid);
+      if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, t, src, valid, e);
+      ws_issue_nope_slice<ROPE>(lds, t, src, valid, e);
+      if (t == 1) tile1_full = valid == kKeys;
+    }
+    if (tile1_full) wait_vmcnt<kCopies>();   // tile 0 has landed; tile 1 may be in flight
+    else wait_vmcnt<0>();
 
-    // V^T lane bases of the two dv blocks (2e, 2e + 1)
-    const int vt0 = vt_lane_base(lane, (2 * e) & 7), vt1 = vt_lane_base(lane, (2 * e + 1) & 7);
-    const int vhi = 256 * ((2 * e) >> 3);   // dv blocks 8..15: the upper half of each nope row
+    // V^T lane base (slice layout): lane group g = lane / 16 reads chunk
+    // 2 j + (g & 1) of dv block 2e + j, key 16 u + tk, tk = tr_key(sup / 2, h),
+    // bytes 8 (sup & 1) .. +7 of the chunk (sup = lane % 16); block 2e + 1 is
+    // block 2e's address ^ 32
+    int vb;
+    {
+      const int sup = lane & 15, tk = tr_key(sup >> 1, h);
+      vb = e * 4096 + tk * 64 + 16 * (((lane >> 4) & 1) ^ ((tk >> 2) & 3)) + 8 * (sup & 1);
+    }
 
     // O^T accumulators: O[j][r] = dv block 2e + j of row block r (VGPRs)
     f32x16 O[2][kSWaves];
@@ -398,33 +431,42 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
 #pragma unroll
       for (int r = 0; r < kSWaves; ++r) O[j][r] = f32x16{};
 
-    int bufp = 2;   // ring buffer of tile k-1
+    int bufp = 2;   // ring slot of tile k-1 (= slot of tile k+2)
     for (int k = 0; k <= ntiles; ++k) {
-      wait_vmcnt<0>();   // this wave's copies of tile k have landed
-      __syncthreads();
-      const int buf_next = bufp == 0 ? 2 : bufp - 1;   // (k + 1) % 3
-      if (k + 1 < ntiles) {
-        if (((k + 1) & 63) == 0) {   // next 64 page ids
-          pages_v = page_of_lane(u0 + k + 1 + lane);
+      __syncthreads();   // tile k has landed in every wave's share
+      const bool next2 = k + 2 < ntiles;
+      int valid2 = 0;
+      const uint8_t* src2 = nullptr;
+      if (next2) {
+        if (((k + 2) & 63) == 0) {   // next 64 page ids
+          pages_v = page_of_lane(u0 + k + 2 + lane);
           wait_vmcnt<0>();
         }
-        issue(k + 1, buf_next);
+        src2 = tile_src(k + 2, valid2);
+        if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, bufp, src2, valid2, e);   // S^T(k-1) released it
       }
+      i32x8 vr[2];
       if (k > 0) {
-        const int pp = (k - 1) & 1;
-        const i32x4 fl = *reinterpret_cast<const i32x4*>(xflag + 4 * pp);
         const uint8_t* vnope = lds + bufp * kNopeRegion;
-        const uint8_t* pprev = xp + pp * WsX::p_bytes;
-        i32x8 vr[2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const i32x2 v0 = lds_tr8(vnope, vt0 + 8192 * u + vhi);
-          const i32x2 v1 = lds_tr8(vnope, vt1 + 8192 * u + vhi);
+          const i32x2 v0 = lds_tr8(vnope, vb + 1024 * u);
+          const i32x2 v1 = lds_tr8(vnope, (vb ^ 32) + 1024 * u);
           vr[0][2 * u] = v0.x;
           vr[0][2 * u + 1] = v0.y;
           vr[1][2 * u] = v1.x;
           vr[1][2 * u + 1] = v1.y;
         }
+      }
+      if (next2) {
+        // this wave's slice of tile k-1 has been read: refill it with tile k+2
+        if (k > 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vr[0]), "+v"(vr[1]) :: "memory");
+        ws_issue_nope_slice<ROPE>(lds, bufp, src2, valid2, e);
+      }
+      if (k > 0) {
+        const int pp = (k - 1) & 1;
+        const i32x4 fl = *reinterpret_cast<const i32x4*>(xflag + 4 * pp);
+        const uint8_t* pprev = xp + pp * WsX::p_bytes;
         // rescale O for the rows whose max tile k-1 raised (rare), before its products
         if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
           asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -452,6 +494,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // tile k+1 must have landed before the next barrier; tile k+2 may stay in flight
+      if (next2 && valid2 == kKeys) wait_vmcnt<kCopies>();
+      else wait_vmcnt<0>();
       bufp = bufp == kBufs - 1 ? 0 : bufp + 1;
     }
 
@@ -499,6 +544,48 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       }
     }
   }
+}
+
+// Gather check of the slice layout: one workgroup of eight waves per
+// (sequence, page unit) runs the PV-waves' copies into slot 0 and writes the
+// tile back in logical row order.
+template <int ROPE>
+__global__ __launch_bounds__(512) void debug_gather_ws_kernel(const uint8_t* kv, const int32_t* block_table,
+                                                              const int32_t* seq_lens, int max_pages, int num_pages,
+                                                              uint8_t* dense_out) {
+  constexpr int RB = kNope + 2 * ROPE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Tile<ROPE>::lds_bytes];
+  const int e = wave_id();
+  const int b = blockIdx.x / max_pages, unit = blockIdx.x % max_pages;
+  int sk = seq_lens[b];
+  sk = max(0, min(sk, max_pages * kKeys));
+  const int page = block_table[(long)b * max_pages + unit];
+  const bool page_ok = page >= 0 && page < num_pages;
+  const int valid = page_ok ? max(0, min(kKeys, sk - unit * kKeys)) : 0;
+  const uint8_t* src = kv + (long)(page_ok ? page : 0) * kKeys * RB;
+  if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 0, src, valid, e);
+  ws_issue_nope_slice<ROPE>(lds, 0, src, valid, e);
+  wait_tile_and_sync();
+  uint8_t* dst = dense_out + ((long)b * max_pages + unit) * kKeys * RB;
+  for (int idx = threadIdx.x; idx < kKeys * (RB / 16); idx += 512) {
+    const int r = idx / (RB / 16), c = idx % (RB / 16);
+    const int off = c < 32 ? (c >> 2) * 4096 + r * 64 + 16 * ((c & 3) ^ ((r >> 2) & 3))
+                           : kRopeBase + r * 128 + (swz_rope(r, c - 32) << 4);
+    *reinterpret_cast<i32x4*>(dst + r * RB + c * 16) = lds_ld16(lds, off);
+  }
+}
+
+hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table, const int32_t* seq_lens,
+                                  int32_t batch, int32_t max_pages, int32_t num_pages, int32_t d_rope,
+                                  uint8_t* dense_out, hipStream_t st) {
+  const dim3 grid((unsigned)(batch * max_pages));
+  if (d_rope == 64)
+    hipLaunchKernelGGL((debug_gather_ws_kernel<64>), grid, dim3(512), 0, st, kv, block_table, seq_lens, max_pages,
+                       num_pages, dense_out);
+  else
+    hipLaunchKernelGGL((debug_gather_ws_kernel<0>), grid, dim3(512), 0, st, kv, block_table, seq_lens, max_pages,
+                       num_pages, dense_out);
+  return hipGetLastError();
 }
 
 bool decode_ws_eligible(const DecodeLaunch& d) {

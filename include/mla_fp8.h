@@ -27,7 +27,8 @@
  *   lse          f32    [batch, s_q, h_q]          natural log; -inf for a row
  *                                                  with no visible key (out = 0)
  *   workspace    device scratch of mla_fp8_decode_workspace_size() bytes when
- *                the resolved split count is > 1 (may be NULL otherwise)
+ *                the resolved split count is > 1 (may be NULL otherwise);
+ *                calls that share a workspace must be ordered on one stream
  *
  * Semantics not fixed by the source pages, as implemented:
  *   softmax_scale <= 0 selects 1/sqrt(d_nope + d_rope); causal rows are
@@ -258,6 +259,13 @@ MLA_API int32_t mla_fp8_debug_quantize_q(const void* q, int32_t rows, int32_t ro
 MLA_API int32_t mla_fp8_debug_gather(const mla_params* p, const void* kv_cache,
                                      const int32_t* block_table, const int32_t* seq_lens,
                                      void* dense_out, void* hip_stream);
+
+/* The same check for the tile loader of the role-split fp8 kernel (its nope
+ * bytes in 4 KiB dv slices): copies through that loader (global -> LDS ->
+ * global) in the layout and with the zero-fill of mla_fp8_debug_gather. */
+MLA_API int32_t mla_fp8_debug_gather_ws(const mla_params* p, const void* kv_cache,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        void* dense_out, void* hip_stream);
 
 /* Matrix-core throughput probe: `blocks` workgroups of 256 threads, each wave
  * issuing 4 * iters independent 32x32 MFMAs (MLA_DOT_FP8: 32x32x64 fp8,

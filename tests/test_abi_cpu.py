@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 15
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
     assert set(names) <= exported
@@ -126,6 +126,8 @@ def test_workspace_size(L):
     assert mla.workspace_size(p, 1) == 0
     frags = 4 * 64 * 4
     assert mla.workspace_size(p, 4) == frags * (16 * 64 * 16 * 2 + 32 * 4)
+    q = good(batch=3, s_q=1, h_q=16)                  # one row block per sequence
+    assert mla.workspace_size(q, 2) == 2 * 3 * (16 * 64 * 16 * 2 + 32 * 4)
     assert mla.workspace_size(good(batch=0), 4) == 0
 
 
@@ -173,6 +175,8 @@ def test_debug_exports_check_arguments(L):
                                       None) == mla.MLA_ERR_SHAPE
     assert L.mla_fp8_bench_stream_read(ctypes.c_void_p(16), 17, ctypes.c_void_p(16), None) == mla.MLA_ERR_SHAPE
     assert L.mla_fp8_debug_gather(ctypes.byref(good(h_kv=3)), None, None, None, None, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_fp8_debug_gather_ws(ctypes.byref(good(h_kv=3)), None, None, None, None, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_fp8_debug_gather_ws(ctypes.byref(good()), None, None, None, None, None) == mla.MLA_ERR_NULL
 
 
 # ---- quantize-on-write: host checks (every call returns before a launch) ----

@@ -61,11 +61,12 @@ def test_query_quantization_matches_oracle(shape):
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("mtp", {"batch": 3, "seq_len": [8196, 65, 0]}),
                                      ("sparse", {"batch": 2, "seq_len": 4096, "topk": 64}),
                                      ("tiny", {"batch": 2, "seq_len": [1, 127]})])
-def test_paged_gather_is_bytewise_exact(name, kw):
+@pytest.mark.parametrize("loader", ["dense", "ws"])
+def test_paged_gather_is_bytewise_exact(name, kw, loader):
     w = workloads.make(name, **kw)
     kv = torch.from_numpy(w.kv_cache).to(DEV)
     dense = mla.debug_gather(kv, torch.from_numpy(w.block_table).to(DEV),
-                             torch.from_numpy(w.seq_lens).to(DEV)).cpu().numpy()
+                             torch.from_numpy(w.seq_lens).to(DEV), loader=loader).cpu().numpy()
     b, mp = w.block_table.shape
     for bi in range(b):
         sk = int(w.seq_lens[bi])

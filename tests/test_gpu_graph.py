@@ -20,7 +20,7 @@ def test_captured_decode_replays_bit_exact(dot):
     t = gu.device_inputs(w)
     p = mla.params_for(t["q"], t["kv"], t["bt"], causal=True, dot=dot)
     splits = mla.resolve_splits(p, 0, mla.cu_count())
-    ws = torch.empty(max(mla.workspace_size(p, splits), 16), dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(max(mla.workspace_size(p, splits), 16), dtype=torch.uint8, device="cuda:0")
     out = torch.empty((4, 2, 64, 512), dtype=torch.bfloat16, device="cuda:0")
     lse = torch.empty((4, 2, 64), dtype=torch.float32, device="cuda:0")
     kw = dict(num_splits=splits, dot=dot, causal=True, out=out, lse=lse, workspace=ws)
