@@ -63,6 +63,15 @@ struct WsX {
   static constexpr int bytes = fin_off + kSWaves * 32 * 4;
 };
 
+// The lane id from the exec-mask bit count, as volatile asm: recomputed where
+// it is used inside a tile loop rather than kept (and, at three waves per
+// SIMD, spilled and reloaded from scratch memory every tile).
+__device__ inline int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Max of x over lanes l and l ^ 32 (the two halves of one query row) with the
 // gfx950 lane swap: no LDS round trip.
 __device__ inline float pair_max_swap(float x) {
@@ -323,7 +332,8 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         // register r of key block kb is key 32 kb + 8 j + 4 ((j + h) & 1) + r % 4
         // (j = r / 4): compile-time offsets against two per-lane limits, so
         // that no per-lane key index is kept across the tile loop
-        const int lim_e = limit - 4 * h, lim_o = limit - 4 * (1 - h);
+        const int hl = fresh_lane() >> 5;
+        const int lim_e = limit - 4 * hl, lim_o = limit - 4 * (1 - hl);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -348,7 +358,10 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         l_run *= alpha;
         // O needs rescaling only where a finite max was raised
         flagged = __ballot(raise && m_run != -INFINITY) != 0ull;
-        if (flagged && h == 0) xalpha[par * (kSWaves * 32) + wave * 32 + n] = alpha;
+        if (flagged) {
+          const int ln = fresh_lane();
+          if (ln < 32) xalpha[par * (kSWaves * 32) + wave * 32 + ln] = alpha;
+        }
         m_run = m_new;
       }
       const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT_FP8>::ps_log2;
@@ -366,10 +379,11 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         pb[q4] = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
       }
       l_run += psum;
-      uint8_t* pdst = xp + par * WsX::p_bytes + wave * 2048 + lane * 16;
+      const int lp = fresh_lane();
+      uint8_t* pdst = xp + par * WsX::p_bytes + wave * 2048 + lp * 16;
       *reinterpret_cast<i32x4*>(pdst) = i32x4{pb[0], pb[1], pb[2], pb[3]};
       *reinterpret_cast<i32x4*>(pdst + 1024) = i32x4{pb[4], pb[5], pb[6], pb[7]};
-      if (lane == 0) xflag[4 * par + wave] = flagged ? 1 : 0;
+      if (lp == 0) xflag[4 * par + wave] = flagged ? 1 : 0;
       buf = buf == kBufs - 1 ? 0 : buf + 1;
     }
 
@@ -474,7 +488,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
 #pragma unroll
           for (int r = 0; r < kSWaves; ++r) {
             if (__builtin_amdgcn_readfirstlane(fl[r])) {
-              const float f = al[r * 32 + n];
+              const float f = al[r * 32 + (fresh_lane() & 31)];
 #pragma unroll
               for (int x = 0; x < 16; ++x) {
                 O[0][r][x] *= f;
@@ -484,10 +498,11 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           }
           asm volatile("s_nop 4" ::: "memory");
         }
+        const int lo16 = fresh_lane() * 16;
 #pragma unroll
         for (int r = 0; r < kSWaves; ++r) {
-          const i32x4 lo = lds_ld16(pprev, r * 2048 + lane * 16);
-          const i32x4 hi = lds_ld16(pprev, r * 2048 + 1024 + lane * 16);
+          const i32x4 lo = lds_ld16(pprev, r * 2048 + lo16);
+          const i32x4 hi = lds_ld16(pprev, r * 2048 + 1024 + lo16);
           const i32x8 pt = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           mfma_fp8_32x32x64(O[0][r], vr[0], pt);
           mfma_fp8_32x32x64(O[1][r], vr[1], pt);
