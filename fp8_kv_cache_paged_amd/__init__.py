@@ -25,6 +25,10 @@ MLA_ERR_UNSUPPORTED = 4
 MLA_ERR_WORKSPACE = 5
 MLA_ERR_ALIGN = 6
 MLA_ERR_HIP = 7
+MLA_ERR_SCRATCH = 8
+
+# fixed device scratch of mla_fp8_decode_noalloc, per GPU
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # kv_dtype codes
 MLA_KV_FP8_E4M3FN = 0
@@ -93,6 +97,8 @@ def lib() -> ctypes.CDLL:
         dec_args = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.mla_fp8_decode.argtypes = dec_args
         L.mla_fp8_decode.restype = i32
+        L.mla_fp8_decode_noalloc.argtypes = dec_args[:11] + [vp]
+        L.mla_fp8_decode_noalloc.restype = i32
         L.mla_fp8_decode_partials.argtypes = dec_args
         L.mla_fp8_decode_partials.restype = i32
         L.mla_fp8_debug_decode_variant.argtypes = dec_args[:-1] + [i32, vp]
@@ -225,6 +231,24 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, s
         fn = L.mla_fp8_decode_partials if partials_only else L.mla_fp8_decode
         st = fn(*args, _stream(stream))
     _check(st, "mla_fp8_decode")
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                   k_scale: torch.Tensor, v_scale: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, *,
+                   num_splits: int = 0, dot: str = "fp8", causal: bool = True, softmax_scale: float = 0.0,
+                   indices: Optional[torch.Tensor] = None, stream=None,
+                   per_token_scales: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_fp8_decode_noalloc: the decode with its split partials in the library's fixed
+    per-GPU scratch (MLA_NOALLOC_SCRATCH_BYTES) instead of a workspace. The caller
+    passes `out` (bf16 [b, s_q, h_q, 512]) and `lse` (f32 [b, s_q, h_q]); nothing is
+    allocated. Calls that overlap on one GPU race on the scratch."""
+    p = params_for(q, kv_cache, block_table, causal=causal, dot=dot, indices=indices,
+                   softmax_scale=softmax_scale, per_token_scales=per_token_scales)
+    st = lib().mla_fp8_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), int(num_splits), _ptr(out),
+                                      _ptr(lse), _ptr(indices), _stream(stream))
+    _check(st, "mla_fp8_decode_noalloc")
     return out, lse
 
 

@@ -19,7 +19,7 @@ LIB_NAME = "libmla_fp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = os.environ.get("MLA_FP8_ARCH", "gfx950")
 
-SOURCES = ["mla_decode.hip", "mla_decode_ws.hip", "quantize.hip", "probes.hip", "host.cpp"]
+SOURCES = ["mla_decode.hip", "mla_decode_ws.hip", "quantize.hip", "probes.hip", "noalloc.hip", "host.cpp"]
 
 # Packed fp32 VALU instructions are switched off for all device code: hipcc
 # would otherwise form v_pk_* fp32 ops from float2 arithmetic by itself.

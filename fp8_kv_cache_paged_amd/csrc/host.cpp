@@ -108,10 +108,14 @@ int32_t device_cu_count() {
   return cus;
 }
 
+}  // namespace
+
+namespace mla {
+
 int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
                     const int32_t* seq_lens, const float* k_scale, const float* v_scale, int32_t num_splits,
                     void* out, float* lse, const int32_t* indices, void* ws, size_t ws_bytes, void* stream,
-                    bool with_combine, int32_t variant) {
+                    bool with_combine, int32_t variant, WorkspaceFn supply) {
   int32_t st = validate(p);
   if (st != MLA_OK) return st;
   if (q == nullptr || kv_cache == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr ||
@@ -131,6 +135,10 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   const int32_t splits = resolve(*p, num_splits, cus);
   if (splits < 1) return -splits;
   const size_t need = workspace(*p, splits);
+  if (supply != nullptr) {
+    st = supply(need, &ws, &ws_bytes);
+    if (st != MLA_OK) return st;
+  }
   if (need > 0) {
     if (ws == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return MLA_ERR_ALIGN;
@@ -183,7 +191,7 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   return MLA_OK;
 }
 
-}  // namespace
+}  // namespace mla
 
 extern "C" {
 
@@ -205,8 +213,8 @@ MLA_API int32_t mla_fp8_decode(const mla_params* p, const void* q, const void* k
                                const float* v_scale, int32_t num_splits, void* out, float* lse,
                                const int32_t* indices, void* workspace_ptr, size_t workspace_bytes,
                                void* hip_stream) {
-  return decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
-                     workspace_ptr, workspace_bytes, hip_stream, true, 0);
+  return mla::decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
+                     workspace_ptr, workspace_bytes, hip_stream, true, 0, nullptr);
 }
 
 MLA_API int32_t mla_fp8_debug_decode_variant(const mla_params* p, const void* q, const void* kv_cache,
@@ -215,8 +223,8 @@ MLA_API int32_t mla_fp8_debug_decode_variant(const mla_params* p, const void* q,
                                              void* out, float* lse, const int32_t* indices, void* workspace_ptr,
                                              size_t workspace_bytes, int32_t variant, void* hip_stream) {
   if (variant & ~(MLA_VARIANT_GATHER_V | MLA_VARIANT_ROWS | MLA_VARIANT_DV_SPLIT)) return MLA_ERR_SHAPE;
-  return decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
-                     workspace_ptr, workspace_bytes, hip_stream, true, variant);
+  return mla::decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
+                     workspace_ptr, workspace_bytes, hip_stream, true, variant, nullptr);
 }
 
 MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, const void* kv_cache,
@@ -224,8 +232,8 @@ MLA_API int32_t mla_fp8_decode_partials(const mla_params* p, const void* q, cons
                                         const float* k_scale, const float* v_scale, int32_t num_splits,
                                         void* out, float* lse, const int32_t* indices, void* workspace_ptr,
                                         size_t workspace_bytes, void* hip_stream) {
-  return decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
-                     workspace_ptr, workspace_bytes, hip_stream, false, 0);
+  return mla::decode_impl(p, q, kv_cache, block_table, seq_lens, k_scale, v_scale, num_splits, out, lse, indices,
+                     workspace_ptr, workspace_bytes, hip_stream, false, 0, nullptr);
 }
 
 MLA_API const char* mla_fp8_status_string(int32_t status) {
@@ -238,6 +246,7 @@ MLA_API const char* mla_fp8_status_string(int32_t status) {
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_ALIGN: return "a pointer is misaligned";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_SCRATCH: return "the call needs more workspace than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

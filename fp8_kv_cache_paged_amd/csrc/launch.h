@@ -1,12 +1,26 @@
-// Internal interface between the C-ABI host layer (host.cpp) and the HIP
-// kernels (mla_decode.hip). Not installed; include/mla_fp8.h is the public ABI.
+// Internal interface between the C-ABI host layer (host.cpp, noalloc.hip) and
+// the HIP kernels (mla_decode.hip, mla_decode_ws.hip). Not installed; include/mla_fp8.h is the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/mla_fp8.h"
+
 namespace mla {
+
+// Supplies the workspace of a decode once its size is known (need bytes, 0
+// when the resolved split count is 1): sets *ws and *ws_bytes, or returns a
+// status that ends the call before any launch.
+using WorkspaceFn = int32_t (*)(size_t need, void** ws, size_t* ws_bytes);
+
+// The decode entry points' common body (host.cpp): host checks, split plan,
+// launches. supply may be null (the caller's ws, ws_bytes are used as given).
+int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, const float* k_scale, const float* v_scale, int32_t num_splits,
+                    void* out, float* lse, const int32_t* indices, void* ws, size_t ws_bytes, void* stream,
+                    bool with_combine, int32_t variant, WorkspaceFn supply);
 
 // Everything a decode launch needs, resolved and validated on the host.
 struct DecodeLaunch {

@@ -42,7 +42,9 @@
  *   converts the cache bytes to bf16 exactly.
  *
  * Ownership, streams and threads: the library never allocates, frees or
- * synchronizes device memory. Every kernel is enqueued on the caller's
+ * synchronizes device memory, apart from one fixed device array per GPU that
+ * the loader reserves for mla_fp8_decode_noalloc (MLA_NOALLOC_SCRATCH_BYTES,
+ * held until the process ends). Every kernel is enqueued on the caller's
  * hip_stream (NULL = the default stream). No mutable global state beyond a
  * per-device cache of the compute-unit count; calls are thread-safe. Results
  * are deterministic: the same inputs and split count give bitwise equal
@@ -78,6 +80,8 @@ extern "C" {
 #define MLA_ERR_WORKSPACE 5    /* workspace missing or too small */
 #define MLA_ERR_ALIGN 6        /* a pointer is not aligned as required */
 #define MLA_ERR_HIP 7          /* the HIP runtime reported an error */
+#define MLA_ERR_SCRATCH 8      /* mla_fp8_decode_noalloc: the call needs more
+                                  workspace than MLA_NOALLOC_SCRATCH_BYTES */
 
 /* kv_dtype codes. The OCP e4m3fn encoding (or a uint8 view of it) is read
  * by both dot modes. gfx942's e4m3fnuz (bias 8, largest magnitude 240, NaN
@@ -163,6 +167,26 @@ MLA_API int32_t mla_fp8_decode(const mla_params* p, const void* q, const void* k
                                const float* k_scale, const float* v_scale, int32_t num_splits,
                                void* out, float* lse, const int32_t* indices, void* workspace,
                                size_t workspace_bytes, void* hip_stream);
+
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Arguments and results as for mla_fp8_decode, without the
+ * workspace: the split partials go to a fixed device array of the library
+ * (MLA_NOALLOC_SCRATCH_BYTES per GPU, 256-byte aligned, its address looked up
+ * once per device on the first call that needs it). A call whose
+ * mla_fp8_decode_workspace_size() exceeds that size returns MLA_ERR_SCRATCH
+ * before any launch (a smaller explicit num_splits lowers the need; 1 needs
+ * none). The call allocates nothing: no
+ * hipMalloc, no library routine that allocates. Every call on one GPU shares
+ * that GPU's array, whose contents need no clearing (each call overwrites the
+ * partials it reads): calls that overlap on one GPU (two streams, or two
+ * threads without ordering) race on it and give unspecified results; calls
+ * ordered on one stream are safe. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+MLA_API int32_t mla_fp8_decode_noalloc(const mla_params* p, const void* q, const void* kv_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const float* k_scale, const float* v_scale, int32_t num_splits,
+                                       void* out, float* lse, const int32_t* indices, void* hip_stream);
 
 /* First stage only (timing and tests): with a resolved split count > 1 it
  * writes the per-split partials into the workspace and launches no combine;

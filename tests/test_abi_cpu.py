@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_symbols()
-    assert len(names) == 15
+    assert len(names) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
     assert set(names) <= exported
@@ -89,8 +89,8 @@ def test_validate_null_params(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
-        assert mla.status_string(s)
+    for s in range(9):
+        assert mla.status_string(s) != "unknown status"
     assert mla.status_string(99) == "unknown status"
 
 
@@ -155,6 +155,20 @@ def test_decode_rejects_before_any_launch(L):
     st = L.mla_fp8_decode(ctypes.byref(p), *[ctypes.c_void_p(16)] * 6, 2, ctypes.c_void_p(16),
                           ctypes.c_void_p(16), None, None, 0, None)
     assert st == mla.MLA_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_before_any_launch(L):
+    # host pointers that are never dereferenced; explicit split counts, so no HIP call
+    v = ctypes.c_void_p
+    p = good(batch=1024, s_q=2, h_q=64)
+    assert mla.workspace_size(p, 4) > mla.MLA_NOALLOC_SCRATCH_BYTES
+    args = [ctypes.byref(p)] + [v(16)] * 6
+    assert L.mla_fp8_decode_noalloc(*args, 4, v(16), v(16), None, None) == mla.MLA_ERR_SCRATCH
+    assert L.mla_fp8_decode_noalloc(*args, 4, None, v(16), None, None) == mla.MLA_ERR_NULL
+    assert L.mla_fp8_decode_noalloc(*args, 4, v(24), v(16), None, None) == mla.MLA_ERR_ALIGN
+    bad = good(h_kv=2)
+    assert L.mla_fp8_decode_noalloc(ctypes.byref(bad), *[v(16)] * 6, 4, v(16), v(16), None,
+                                    None) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_decode_variant_rejects_unknown_bits_before_any_launch(L):
