@@ -1246,20 +1246,55 @@ __global__ void debug_decode_kernel(const uint8_t* codes, float* out_f32, uint16
   }
 }
 
-// One wave per 32 rows, the same lane split as the decode kernel.
+// Query quantization check: the decode's two quantizers on the same rows.
+// Each workgroup takes 16 rows with the lane-quad quantizer of the role-split
+// kernel (its codes and exponents are written out) and quantizes them again
+// with the half-row quantizer of the other kernels; a row where the two
+// disagree reports the exponent INT32_MIN, which no row can have.
 __global__ __launch_bounds__(64) void debug_quantize_q_kernel(const uint16_t* q, int rows, int row_len,
                                                               uint8_t* codes, int32_t* exps) {
-  const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
-  const int row = blockIdx.x * 32 + n;
+  __shared__ __attribute__((aligned(16))) uint8_t lc[16 * kNope];
+  __shared__ int le[16], bad[16];
+  const int lane = threadIdx.x;
+  const int r4 = lane >> 2, qq = lane & 3;
+  const int row = blockIdx.x * 16 + r4;
   const bool ok = row < rows;
-  i32x8 qn[8];
-  int e;
-  stage_q_fp8(q + (long)(ok ? row : 0) * row_len, ok, h, qn, e);
+  {
+    const uint16_t* src = q + (long)(ok ? row : 0) * row_len + 8 * qq;
+    i32x4 raw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const i32x4*>(src + 32 * i);
+    uint2 c[16];
+    const int e = quantize_q_quad(raw, c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<uint2*>(lc + r4 * kNope + 8 * (4 * i + qq)) = c[i];
+    if (qq == 0) {
+      le[r4] = e;
+      bad[r4] = 0;
+    }
+  }
+  __syncthreads();
+  {
+    const int n = lane & 31, h = lane >> 5, r = n & 15;
+    const int row2 = blockIdx.x * 16 + r;
+    const bool ok2 = row2 < rows;
+    i32x8 qn[8];
+    int e2;
+    stage_q_fp8(q + (long)(ok2 ? row2 : 0) * row_len, ok2, h, qn, e2);
+    bool same = e2 == le[r];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) same = same && qn[t][d] == *reinterpret_cast<const int*>(lc + r * kNope + 64 * t + 32 * h + 4 * d);
+    if (!same) bad[r] = 1;
+  }
+  __syncthreads();
   if (!ok) return;
-  for (int t = 0; t < 8; ++t)
-    for (int d = 0; d < 8; ++d)
-      *reinterpret_cast<int*>(codes + (long)row * kNope + 64 * t + 32 * h + 4 * d) = qn[t][d];
-  if (h == 0) exps[row] = e;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    *reinterpret_cast<uint2*>(codes + (long)row * kNope + 8 * (4 * i + qq)) =
+        *reinterpret_cast<const uint2*>(lc + r4 * kNope + 8 * (4 * i + qq));
+  if (qq == 0) exps[row] = bad[r4] ? INT32_MIN : le[r4];
 }
 
 // Gather check: one workgroup per (sequence, page unit) runs the decode
@@ -1446,7 +1481,7 @@ hipError_t launch_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint
 
 hipError_t launch_debug_quantize_q(const uint16_t* q, int32_t rows, int32_t row_len, uint8_t* codes,
                                    int32_t* exps, hipStream_t st) {
-  hipLaunchKernelGGL(debug_quantize_q_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(64), 0, st, q,
+  hipLaunchKernelGGL(debug_quantize_q_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(64), 0, st, q,
                      rows, row_len, codes, exps);
   return hipGetLastError();
 }

@@ -63,6 +63,23 @@ struct WsX {
   static constexpr int bytes = fin_off + kSWaves * 32 * 4;
 };
 
+// LDS that nothing touches before the first tile barrier, where the PV-waves
+// stage the quantized query for the S-waves: the third ring slot's nope bytes
+// (row blocks 0 and 1, 16 KiB each), its rope bytes and the exchange area
+// (row blocks 2 and 3), then 128 row exponents. Row n of a block holds its
+// 512 codes with 16-byte chunk j at position j ^ n.
+template <int ROPE>
+struct WsQ {
+  static constexpr int a_off = 2 * kNopeRegion;
+  static constexpr int b_off = Tile<ROPE>::lds_bytes - (ROPE > 0 ? kRopeRegion : 0);
+  static constexpr int exp_off = b_off + 2 * 16384;
+  static constexpr int end = exp_off + kSWaves * 32 * 4;
+  static constexpr int lds_bytes = end > Tile<ROPE>::lds_bytes + WsX::bytes ? end : Tile<ROPE>::lds_bytes + WsX::bytes;
+  static_assert(kBufs == 3 && a_off + 2 * 16384 <= kRopeBase, "row blocks 0 and 1 fit the third nope slot");
+  static_assert(ROPE == 0 || b_off == kRopeBase + 2 * kRopeRegion, "row blocks 2 and 3 start at the third rope slot");
+  static_assert(lds_bytes <= 160 * 1024, "LDS");
+};
+
 // The lane id from the exec-mask bit count, as volatile asm: recomputed where
 // it is used inside a tile loop rather than kept (and, at three waves per
 // SIMD, spilled and reloaded from scratch memory every tile).
@@ -144,12 +161,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), a
 void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   constexpr int D = kNope + ROPE;   // q row length
   constexpr long RB = kNope + 2 * ROPE;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_[Tile<ROPE>::lds_bytes + WsX::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes];
   uint8_t* const lds = lds_;
   uint8_t* const xp = lds + Tile<ROPE>::lds_bytes;
   float* const xalpha = reinterpret_cast<float*>(xp + 2 * WsX::p_bytes);
   int* const xflag = reinterpret_cast<int*>(xp + WsX::flag_off);
   float* const xfin = reinterpret_cast<float*>(xp + WsX::fin_off);
+  // prologue only: the quantized query rows of row block w, then the exponents
+  auto qstage = [&](int w) -> uint8_t* { return lds + (w < 2 ? WsQ<ROPE>::a_off + w * 16384 : WsQ<ROPE>::b_off + (w - 2) * 16384); };
+  int* const qexp = reinterpret_cast<int*>(lds + WsQ<ROPE>::exp_off);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -181,52 +201,19 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     const bool q_ok = row_ok && wave_active;
     const uint16_t* qsrc = q_ok ? q + qrow_idx * D : q;   // rows outside the problem read row 0, zeroed below
 
-    // Query row n: two passes over its 512 nope values (a 128-register copy
-    // of the raw row next to its codes would not fit three waves per SIMD):
-    // the row max, then the codes, from a second read of the same bytes
-    // (through a pointer the compiler cannot equate with the first, so that
-    // it does not keep the first read's registers alive instead).
+    // The query's rope values and the page ids come from global memory; its
+    // nope part, quantized by the PV-waves during the prologue, from LDS.
     i32x4 qr_raw[ROPE > 0 ? 4 : 1];
     if constexpr (ROPE > 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) qr_raw[t] = *reinterpret_cast<const i32x4*>(qsrc + kNope + 16 * t + 8 * h);
     }
     int pages_v = page_of_lane(u0 + lane);
-    // (each pass in groups of two fragments, 32 registers of loads in flight:
-    // issued all at once the loads alone would need 128)
-    float amax = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(qsrc + 64 * t + 32 * h + 8 * k);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo((unsigned)v[d])), fabsf(bf16_hi((unsigned)v[d]))));
-      }
-      if (t & 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    amax = pair_max_swap(amax);
-    const int qe = q_exponent(amax);
-    const int ne = -qe;   // x * 2^-e by exponent adjustment (finite for every bf16 row)
-    const uint16_t* qsrc2 = qsrc;
-    asm volatile("" : "+v"(qsrc2));
-    i32x8 qn[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(qsrc2 + 64 * t + 32 * h + 8 * k);
-        const unsigned w0 = (unsigned)v[0], w1 = (unsigned)v[1], w2 = (unsigned)v[2], w3 = (unsigned)v[3];
-        const int c0 = f32x4_to_fp8x4(ldexpf(bf16_lo(w0), ne), ldexpf(bf16_hi(w0), ne), ldexpf(bf16_lo(w1), ne),
-                                      ldexpf(bf16_hi(w1), ne));
-        const int c1 = f32x4_to_fp8x4(ldexpf(bf16_lo(w2), ne), ldexpf(bf16_hi(w2), ne), ldexpf(bf16_lo(w3), ne),
-                                      ldexpf(bf16_hi(w3), ne));
-        qn[t][2 * k] = q_ok ? c0 : 0;
-        qn[t][2 * k + 1] = q_ok ? c1 : 0;
-        if ((t & 1) && k == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-    const float qk_scale = ldexpf(*k_scale, qe);   // q_scale * k_scale on the nope products
+    const float k_scale_v = *k_scale;
+    const int i_tok = row / a.h_q;
+    const int row_len = row_ok ? (a.causal ? sk - (a.s_q - 1 - i_tok) : sk) : 0;   // keys this row may see
+    wait_vmcnt<0>();
+    asm volatile("" : "+v"(pages_v));
     bf16x8 qr[ROPE > 0 ? 4 : 1];
     if constexpr (ROPE > 0) {
 #pragma unroll
@@ -237,10 +224,23 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         qr[t] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    const int i_tok = row / a.h_q;
-    const int row_len = row_ok ? (a.causal ? sk - (a.s_q - 1 - i_tok) : sk) : 0;   // keys this row may see
-    wait_vmcnt<0>();
-    asm volatile("" : "+v"(pages_v));
+    __syncthreads();   // the quantized query rows are staged
+    // fragment t of lane (n, h): codes of dims 64 t + 32 h .. +31, staged
+    // chunks 4 t + 2 h and 4 t + 2 h + 1 of row n
+    i32x8 qn[8];
+    {
+      const uint8_t* qs = qstage(wave) + n * 512;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const i32x4 lo = lds_ld16(qs, ((4 * t + 2 * h) ^ n) << 4);
+        const i32x4 hi = lds_ld16(qs, ((4 * t + 2 * h + 1) ^ n) << 4);
+        qn[t] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+    }
+    const int qe = qexp[wave * 32 + n];
+    // the staging area is reused once the tile loop starts: reads done first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const float qk_scale = ldexpf(k_scale_v, qe);   // q_scale * k_scale on the nope products
 
     // z (log2 units) = acc * zscale: with rope the nope sums are scaled by
     // q_scale * k_scale in place before the rope products accumulate onto them
@@ -407,6 +407,17 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     const int e = wave - kSWaves;          // dv slice 64e .. 64e + 63 (blocks 2e, 2e + 1)
     constexpr int kCopies = 4 + (ROPE > 0 ? 1 : 0);   // this wave's copies of one full tile
     int pages_v = page_of_lane(u0 + lane);
+    // query staging: this wave quantizes rows 16 e .. 16 e + 15 of the row
+    // group, one per lane quad (quarter qq holds chunks 4 i + qq); rows outside
+    // the problem read row 0 and stage zero codes
+    const int qrl = 16 * e + (lane >> 2), qq = lane & 3;
+    const bool q_ok = rg * (kSWaves * 32) + qrl < a.rows;
+    i32x4 qraw[16];
+    {
+      const uint16_t* qsrc = q + (q_ok ? ((long)g * a.rows + rg * (kSWaves * 32) + qrl) * D : 0) + 8 * qq;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qraw[i] = *reinterpret_cast<const i32x4*>(qsrc + 32 * i);
+    }
     wait_vmcnt<0>();
     asm volatile("" : "+v"(pages_v));
     // keys of tile t that exist (0 for a missing page), and its first cache byte
@@ -425,6 +436,17 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       ws_issue_nope_slice<ROPE>(lds, t, src, valid, e);
       if (t == 1) tile1_full = valid == kKeys;
     }
+    {
+      uint2 codes[16];
+      const int qe = quantize_q_quad(qraw, codes);
+      const int nn = qrl & 31;
+      uint8_t* dst = qstage(qrl >> 5) + nn * 512 + 8 * (qq & 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *reinterpret_cast<uint2*>(dst + (((2 * i + (qq >> 1)) ^ nn) << 4)) = q_ok ? codes[i] : uint2{0u, 0u};
+      if (qq == 0) qexp[qrl] = q_ok ? qe : 0;
+    }
+    __syncthreads();   // the quantized query rows are staged
     if (tile1_full) wait_vmcnt<kCopies>();   // tile 0 has landed; tile 1 may be in flight
     else wait_vmcnt<0>();
 

@@ -674,6 +674,39 @@ __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 q
   quantize_q_fp8(raw, qn, e_out);
 }
 
+// The same quantization with one row per lane quad: quarter qq = lane & 3
+// holds the row's 16-byte chunks 4 i + qq (i = 0..15, 8 bf16 values each) in
+// raw[i]; the row max is reduced over the quad. codes[i] receives the 8 codes
+// of chunk 4 i + qq; returns the row's exponent e. Every quad of the wave
+// must call it (the reduction reads lanes l ^ 1 and l ^ 2).
+__device__ inline int quantize_q_quad(const i32x4 raw[16], uint2 codes[16]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo((unsigned)raw[i][d])), fabsf(bf16_hi((unsigned)raw[i][d]))));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = q_exponent(amax);
+  const int ne = -e;   // exponent adjustment, as in quantize_q_fp8
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const unsigned w0 = (unsigned)raw[i][0], w1 = (unsigned)raw[i][1], w2 = (unsigned)raw[i][2],
+                   w3 = (unsigned)raw[i][3];
+    codes[i].x = (unsigned)f32x4_to_fp8x4(ldexpf(bf16_lo(w0), ne), ldexpf(bf16_hi(w0), ne), ldexpf(bf16_lo(w1), ne),
+                                          ldexpf(bf16_hi(w1), ne));
+    codes[i].y = (unsigned)f32x4_to_fp8x4(ldexpf(bf16_lo(w2), ne), ldexpf(bf16_hi(w2), ne), ldexpf(bf16_lo(w3), ne),
+                                          ldexpf(bf16_hi(w3), ne));
+  }
+  return e;
+}
+
+// The role-split decode (mla_decode_ws.hip): fp8 dots, per-tensor scales,
+// dense, three or more 32-row blocks per key stream.
+bool decode_ws_eligible(const DecodeLaunch& d);
+hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st);
+
 // Softmax bookkeeping runs in the log2 domain with a lazily raised running
 // max: the max used for exponentials is only raised when a tile's max exceeds
 // it by more than tau, so the rescale of the 256 accumulator registers is rare.
@@ -683,11 +716,6 @@ __device__ inline void stage_q_fp8(const uint16_t* qrow, bool ok, int h, i32x8 q
 // kept in the same scaled units. Scaled probabilities stay normal down to
 // p = 2^-11 and representable down to 2^-14 below the running max; tau = 3
 // keeps the rescales of the accumulators rare.
-// The role-split decode (mla_decode_ws.hip): fp8 dots, per-tensor scales,
-// dense, three or more 32-row blocks per key stream.
-bool decode_ws_eligible(const DecodeLaunch& d);
-hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st);
-
 template <int DOT> struct Soft;
 #ifndef MLA_FP8_TAU
 #define MLA_FP8_TAU 3

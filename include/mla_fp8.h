@@ -272,7 +272,10 @@ MLA_API int32_t mla_fp8_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32
 
 /* Runs the fp8-dot path's query quantization on `rows` bf16 rows of length
  * row_len (the first 512 entries of each row are quantized): writes 512 codes
- * per row and the power-of-two exponent e per row (q ~ code * 2^e). */
+ * per row and the power-of-two exponent e per row (q ~ code * 2^e). The
+ * decode kernels quantize with two lane layouts (a row per lane quad, or half
+ * a row per lane); the codes written are the first's, and a row on which the
+ * second disagrees reports e = INT32_MIN. */
 MLA_API int32_t mla_fp8_debug_quantize_q(const void* q, int32_t rows, int32_t row_len,
                                          uint8_t* codes, int32_t* exps, void* hip_stream);
 
