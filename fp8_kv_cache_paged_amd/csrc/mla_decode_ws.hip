@@ -188,7 +188,8 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int u1 = (int)((long)(s + 1) * units / a.splits);
   const int ntiles = u1 - u0;
   const int32_t* bt_row = block_table + (long)g * a.max_pages;
-  auto page_of_lane = [&](int unit) -> int { return unit < u1 ? bt_row[unit] : -1; };
+  // page id of unit u0 + t (uniform: a scalar load)
+  auto page_at = [&](int t) -> int { return u0 + t < u1 ? bt_row[u0 + t] : -1; };
   auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
 
   if (wave < kSWaves) {
@@ -208,12 +209,10 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) qr_raw[t] = *reinterpret_cast<const i32x4*>(qsrc + kNope + 16 * t + 8 * h);
     }
-    int pages_v = page_of_lane(u0 + lane);
     const float k_scale_v = *k_scale;
     const int i_tok = row / a.h_q;
     const int row_len = row_ok ? (a.causal ? sk - (a.s_q - 1 - i_tok) : sk) : 0;   // keys this row may see
     wait_vmcnt<0>();
-    asm volatile("" : "+v"(pages_v));
     bf16x8 qr[ROPE > 0 ? 4 : 1];
     if constexpr (ROPE > 0) {
 #pragma unroll
@@ -255,11 +254,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       __syncthreads();   // tile k landed; P^T of tile k-2's parity is free again
       if (k == ntiles) break;
       const int par = k & 1;
-      if (k > 0 && (k & 63) == 0) {   // next 64 page ids
-        pages_v = page_of_lane(u0 + k + lane);
-        wait_vmcnt<0>();
-      }
-      const int page_cur = __builtin_amdgcn_readlane(pages_v, k & 63);
+      const int page_cur = page_at(k);   // needed after the products
       const uint8_t* nope = lds + buf * kNopeRegion;
       const uint8_t* rope = lds + kRopeBase + buf * kRopeRegion;
       const int unit = u0 + k;
@@ -406,7 +401,6 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // ===================== PV-wave: tile copies, O^T += V^T P^T =====================
     const int e = wave - kSWaves;          // dv slice 64e .. 64e + 63 (blocks 2e, 2e + 1)
     constexpr int kCopies = 4 + (ROPE > 0 ? 1 : 0);   // this wave's copies of one full tile
-    int pages_v = page_of_lane(u0 + lane);
     // query staging: this wave quantizes rows 16 e .. 16 e + 15 of the row
     // group, one per lane quad (quarter qq holds chunks 4 i + qq); rows outside
     // the problem read row 0 and stage zero codes
@@ -419,22 +413,21 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       for (int i = 0; i < 16; ++i) qraw[i] = *reinterpret_cast<const i32x4*>(qsrc + 32 * i);
     }
     wait_vmcnt<0>();
-    asm volatile("" : "+v"(pages_v));
-    // keys of tile t that exist (0 for a missing page), and its first cache byte
-    auto tile_src = [&](int t, int& valid) -> const uint8_t* {
-      const int page = __builtin_amdgcn_readlane(pages_v, t & 63);
+    // keys of tile t that exist (0 for a missing page) and its first cache
+    // byte, for the tile's page id `page`
+    auto tile_src = [&](int t, int page, int& valid) -> const uint8_t* {
       const bool ok = page_valid(page);
       valid = ok ? min(kKeys, sk - (u0 + t) * kKeys) : 0;
       return kv + (long)(ok ? page : 0) * kKeys * RB;
     };
-    // tiles 0 and 1 before the loop; then tile k+2 during iteration k
-    bool tile1_full = false;
-    for (int t = 0; t < 2 && t < ntiles; ++t) {
+    // tile 0 before the loop, tile 1 once tile 0 has landed (which keeps the
+    // prologue's burst of query and tile loads small); then tile k+2 during
+    // iteration k
+    if (ntiles > 0) {
       int valid;
-      const uint8_t* src = tile_src(t, valid);
-      if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, t, src, valid, e);
-      ws_issue_nope_slice<ROPE>(lds, t, src, valid, e);
-      if (t == 1) tile1_full = valid == kKeys;
+      const uint8_t* src = tile_src(0, page_at(0), valid);
+      if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 0, src, valid, e);
+      ws_issue_nope_slice<ROPE>(lds, 0, src, valid, e);
     }
     {
       uint2 codes[16];
@@ -447,8 +440,13 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       if (qq == 0) qexp[qrl] = q_ok ? qe : 0;
     }
     __syncthreads();   // the quantized query rows are staged
-    if (tile1_full) wait_vmcnt<kCopies>();   // tile 0 has landed; tile 1 may be in flight
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();   // tile 0 has landed
+    if (ntiles > 1) {   // tile 1 must land by the end of iteration 0
+      int valid1;
+      const uint8_t* src1 = tile_src(1, page_at(1), valid1);
+      if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 1, src1, valid1, e);
+      ws_issue_nope_slice<ROPE>(lds, 1, src1, valid1, e);
+    }
 
     // V^T lane base (slice layout): lane group g = lane / 16 reads chunk
     // 2 j + (g & 1) of dv block 2e + j, key 16 u + tk, tk = tr_key(sup / 2, h),
@@ -468,17 +466,15 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       for (int r = 0; r < kSWaves; ++r) O[j][r] = f32x16{};
 
     int bufp = 2;   // ring slot of tile k-1 (= slot of tile k+2)
+    int page2 = page_at(2);   // page id of tile k+2, loaded one iteration ahead
     for (int k = 0; k <= ntiles; ++k) {
       __syncthreads();   // tile k has landed in every wave's share
       const bool next2 = k + 2 < ntiles;
       int valid2 = 0;
       const uint8_t* src2 = nullptr;
       if (next2) {
-        if (((k + 2) & 63) == 0) {   // next 64 page ids
-          pages_v = page_of_lane(u0 + k + 2 + lane);
-          wait_vmcnt<0>();
-        }
-        src2 = tile_src(k + 2, valid2);
+        src2 = tile_src(k + 2, page2, valid2);
+        page2 = page_at(k + 3);
         if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, bufp, src2, valid2, e);   // S^T(k-1) released it
       }
       i32x8 vr[2];
