@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmla_fp8.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ASM_DIR = os.path.join(PKG_DIR, "_asm")   # device assembly of the last build
 ARCH = os.environ.get("MLA_FP8_ARCH", "gfx950")
 
 SOURCES = ["mla_decode.hip", "mla_decode_ws.hip", "quantize.hip", "probes.hip", "noalloc.hip", "host.cpp"]
@@ -53,10 +54,21 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
-            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            # .hip sources also keep their gfx950 assembly (-save-temps), which
+            # the wait-state check in tests/ reads
+            lang = ["-x", "hip", "-save-temps=obj"] if src.endswith(".hip") else []
             cmds.append([hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
+        os.makedirs(ASM_DIR, exist_ok=True)
+        for src in SOURCES:
+            if not src.endswith(".hip"):
+                continue
+            stem = src[: -len(".hip")]
+            cands = [f for f in os.listdir(tmp) if f == f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s"]
+            if len(cands) != 1:
+                raise RuntimeError(f"device assembly of {src} not found among the build temporaries")
+            shutil.copyfile(os.path.join(tmp, cands[0]), os.path.join(ASM_DIR, src + ".s"))
         tmp_lib = os.path.join(tmp, LIB_NAME)
         _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
         # atomic replace so that a running process never sees a half-written file

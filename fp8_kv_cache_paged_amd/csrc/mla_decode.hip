@@ -490,6 +490,14 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
     page_next = page_next2;
     row_cur = row_next;
     buf = buf_next;
+    if (k + 1 == ntiles) {
+      // the last P.V products finish before the loop is left (the compiler may
+      // copy the accumulators out at the exit, where it cannot see them busy)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]),
+                     "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]),
+                     "+a"(O[14]), "+a"(O[15]));
+    }
   }
 
   if (!wave_active) return;

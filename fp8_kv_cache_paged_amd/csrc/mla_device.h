@@ -516,15 +516,20 @@ struct LdsBases {
 //    opcode needs none between them;
 //  * VALU reads of an MFMA result: at most 18 wait states for the 16-pass
 //    32x32 MFMAs; s_nop_result gives 32;
-//  * an MFMA reading (as A, B or C) registers a VALU instruction wrote needs a
-//    few wait states; every asm MFMA that may follow VALU writes starts with
-//    s_nop 4.
+//  * an MFMA reading (as A, B or C) registers a VALU instruction wrote needs
+//    2 wait states: every asm MFMA starts with s_nop 1, and the variants named
+//    after_valu with s_nop 4 (the compiler may place an operand's VALU
+//    producer right before the asm statement);
+//  * the compiler also does not know that a register an asm MFMA writes stays
+//    busy for its passes: a value it copies out of an accumulator (say at a
+//    loop exit) must come after an explicit s_nop_result.
+// tests/test_asm_hazards.py checks these windows on the built assembly.
 
 __device__ inline void mfma_fp8_32x32x64(f32x16& acc, const i32x8& a, const i32x8& b) {
-  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_bf16_32x32x16(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_bf16_32x32x16_after_valu(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
@@ -532,10 +537,10 @@ __device__ inline void mfma_bf16_32x32x16_after_valu(f32x16& acc, const bf16x8& 
 // First product of an accumulator chain: C = 0 as an inline constant, so no
 // VALU zeroing (and no wait states after it) is needed.
 __device__ inline void mfma_fp8_32x32x64_first(f32x16& acc, const i32x8& a, const i32x8& b) {
-  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_bf16_32x32x16_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_bf16_32x32x16_first_after_valu(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
@@ -563,7 +568,7 @@ __device__ inline void s_nop_result2(f32x16& a0, f32x16& a1) {
 }
 // O^T += V^T P^T with the accumulator pinned to AGPRs ("a" operands).
 __device__ inline void mfma_fp8_32x32x64_acc(f32x16& acc, const i32x8& a, const i32x8& b) {
-  asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_fp8_32x32x64_acc_after_valu(f32x16& acc, const i32x8& a, const i32x8& b) {
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
