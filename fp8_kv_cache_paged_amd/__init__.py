@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.mla_fp8_status_string.restype = ctypes.c_char_p
         L.mla_fp8_debug_decode_e4m3fn.argtypes = [vp, vp, vp, i32, vp]
         L.mla_fp8_debug_decode_e4m3fn.restype = i32
+        L.mla_fp8_debug_fnuz_to_e4m3fn.argtypes = [vp, vp, i32, vp]
+        L.mla_fp8_debug_fnuz_to_e4m3fn.restype = i32
         L.mla_fp8_debug_quantize_q.argtypes = [vp, i32, i32, vp, vp, vp]
         L.mla_fp8_debug_quantize_q.restype = i32
         L.mla_fp8_debug_gather.argtypes = [P, vp, vp, vp, vp, vp]
@@ -260,6 +262,14 @@ def debug_decode_e4m3fn(codes: torch.Tensor, stream=None) -> Tuple[torch.Tensor,
     _check(lib().mla_fp8_debug_decode_e4m3fn(_ptr(codes), _ptr(f), _ptr(bb), n, _stream(stream)),
            "mla_fp8_debug_decode_e4m3fn")
     return f, bb
+
+
+def debug_fnuz_to_e4m3fn(codes: torch.Tensor, stream=None) -> torch.Tensor:
+    """The fp8-dot path's e4m3fnuz -> e4m3fn byte transcoding on a uint8 device tensor."""
+    out = torch.empty_like(codes)
+    _check(lib().mla_fp8_debug_fnuz_to_e4m3fn(_ptr(codes), _ptr(out), codes.numel(), _stream(stream)),
+           "mla_fp8_debug_fnuz_to_e4m3fn")
+    return out
 
 
 def debug_quantize_q(q: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -40,8 +40,10 @@ int32_t validate(const mla_params* p) {
     case MLA_KV_UINT8:
       break;
     case MLA_KV_FP8_E4M3FNUZ:
-      // decoded to bf16 in registers; the fp8 matrix cores read OCP codes only
-      if (p->dot != MLA_DOT_BF16 || p->kv_scale_per_token != 0) return MLA_ERR_UNSUPPORTED;
+      // per-tensor scales; bf16 dots decode the codes in registers, fp8 dots
+      // (dense only) read them as OCP codes at twice their value
+      if (p->kv_scale_per_token != 0) return MLA_ERR_UNSUPPORTED;
+      if (p->dot == MLA_DOT_FP8 && p->topk > 0) return MLA_ERR_UNSUPPORTED;
       break;
     case MLA_KV_FP8_E5M2:
     case MLA_KV_INT8:
@@ -172,6 +174,8 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   d.part_o = need > 0 ? static_cast<uint16_t*>(ws) : nullptr;
   d.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + frags * 16 * 64 * 16 * sizeof(uint16_t))
                         : nullptr;
+  // the fp8-dot read of an fnuz cache exists in the default kernel only
+  if (variant != 0 && p->kv_dtype == MLA_KV_FP8_E4M3FNUZ && p->dot == MLA_DOT_FP8) return MLA_ERR_UNSUPPORTED;
   d.gather_v = (variant & MLA_VARIANT_GATHER_V) != 0;
   d.rows_kernel = (variant & MLA_VARIANT_ROWS) != 0;
   d.dv_split_kernel = (variant & MLA_VARIANT_DV_SPLIT) != 0;
@@ -294,6 +298,15 @@ MLA_API int32_t mla_fp8_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32
   if (n == 0) return MLA_OK;
   return mla::launch_debug_decode_e4m3fn(codes, out_f32, out_bf16, n, static_cast<hipStream_t>(hip_stream)) ==
                  hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+MLA_API int32_t mla_fp8_debug_fnuz_to_e4m3fn(const uint8_t* codes, uint8_t* out, int32_t n, void* hip_stream) {
+  if (codes == nullptr || out == nullptr) return MLA_ERR_NULL;
+  if (n < 0) return MLA_ERR_SHAPE;
+  if (n == 0) return MLA_OK;
+  return mla::launch_debug_fnuz_to_ocp(codes, out, n, static_cast<hipStream_t>(hip_stream)) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
 }

@@ -75,6 +75,7 @@ hipError_t launch_quantize_kv(const QuantizeLaunch& d, hipStream_t stream);
 
 hipError_t launch_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint16_t* out_bf16,
                                       int32_t n, hipStream_t stream);
+hipError_t launch_debug_fnuz_to_ocp(const uint8_t* codes, uint8_t* out, int32_t n, hipStream_t stream);
 hipError_t launch_debug_quantize_q(const uint16_t* q, int32_t rows, int32_t row_len,
                                    uint8_t* codes, int32_t* exps, hipStream_t stream);
 hipError_t launch_debug_gather(const uint8_t* kv, const int32_t* block_table,

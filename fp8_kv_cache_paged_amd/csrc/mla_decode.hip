@@ -1254,6 +1254,17 @@ __global__ void debug_decode_kernel(const uint8_t* codes, float* out_f32, uint16
   }
 }
 
+// The fp8-dot path's e4m3fnuz -> e4m3fn transcoding (fnuz4_to_ocp4) on n
+// bytes, four per thread.
+__global__ void debug_fnuz_to_ocp_kernel(const uint8_t* codes, uint8_t* out, int n) {
+  const int base = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (base >= n) return;
+  unsigned v = 0;
+  for (int k = 0; k < 4 && base + k < n; ++k) v |= (unsigned)codes[base + k] << (8 * k);
+  const unsigned r = fnuz4_to_ocp4(v);
+  for (int k = 0; k < 4 && base + k < n; ++k) out[base + k] = (uint8_t)(r >> (8 * k));
+}
+
 // Query quantization check: the decode's two quantizers on the same rows.
 // Each workgroup takes 16 rows with the lane-quad quantizer of the role-split
 // kernel (its codes and exponents are written out) and quantizes them again
@@ -1484,6 +1495,13 @@ hipError_t launch_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32, uint
   const int threads = (n + 3) / 4;
   hipLaunchKernelGGL(debug_decode_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                      codes, out_f32, out_bf16, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_fnuz_to_ocp(const uint8_t* codes, uint8_t* out, int32_t n, hipStream_t st) {
+  const int threads = (n + 3) / 4;
+  hipLaunchKernelGGL(debug_fnuz_to_ocp_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, codes,
+                     out, n);
   return hipGetLastError();
 }
 

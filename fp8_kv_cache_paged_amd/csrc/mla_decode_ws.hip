@@ -156,7 +156,21 @@ __device__ __attribute__((always_inline)) inline void ws_issue_rope(uint8_t* lds
   }
 }
 
-template <int ROPE>
+// gfx942's e4m3fnuz codes turned into OCP e4m3fn codes (fnuz4_to_ocp4), in
+// place in this wave's 4 KiB slice of a landed tile: the fp8 matrix cores read
+// OCP codes only.
+__device__ inline void ws_fnuz_to_ocp_slice(uint8_t* lds, int bufi, int e) {
+  uint8_t* p = lds + bufi * kNopeRegion + e * 4096 + fresh_lane() * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    i32x4 v = *reinterpret_cast<const i32x4*>(p + 16 * i);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = (int)fnuz4_to_ocp4((unsigned)v[d]);
+    *reinterpret_cast<i32x4*>(p + 16 * i) = v;
+  }
+}
+
+template <int ROPE, bool FNUZ>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(3, 3)))
 void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   constexpr int D = kNope + ROPE;   // q row length
@@ -441,6 +455,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     __syncthreads();   // the quantized query rows are staged
     wait_vmcnt<0>();   // tile 0 has landed
+    if constexpr (FNUZ) {
+      if (ntiles > 0) ws_fnuz_to_ocp_slice(lds, 0, e);
+    }
     if (ntiles > 1) {   // tile 1 must land by the end of iteration 0
       int valid1;
       const uint8_t* src1 = tile_src(1, page_at(1), valid1);
@@ -530,6 +547,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       // tile k+1 must have landed before the next barrier; tile k+2 may stay in flight
       if (next2 && valid2 == kKeys) wait_vmcnt<kCopies>();
       else wait_vmcnt<0>();
+      if constexpr (FNUZ) {
+        if (k + 1 < ntiles) ws_fnuz_to_ocp_slice(lds, (k + 1) % kBufs, e);
+      }
       bufp = bufp == kBufs - 1 ? 0 : bufp + 1;
     }
 
@@ -622,17 +642,21 @@ hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table,
 }
 
 bool decode_ws_eligible(const DecodeLaunch& d) {
-  return d.dot == DOT_FP8 && !d.per_token && !d.fnuz && d.topk == 0 && d.row_blocks >= 3 && !d.rows_kernel &&
-         !d.dv_split_kernel && !d.gather_v;
+  if (d.dot != DOT_FP8 || d.per_token || d.topk != 0 || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
+  // an fnuz cache with fp8 dots runs here at any row count (the only kernel that reads it with fp8 dots)
+  return d.fnuz || d.row_blocks >= 3;
 }
 
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
 #define MLA_WS_ARGS d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
-  if (d.d_rope == 64)
-    hipLaunchKernelGGL((mla_decode_ws_kernel<64>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-  else
-    hipLaunchKernelGGL((mla_decode_ws_kernel<0>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+  if (d.d_rope == 64) {
+    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<64, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    else hipLaunchKernelGGL((mla_decode_ws_kernel<64, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+  } else {
+    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<0, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    else hipLaunchKernelGGL((mla_decode_ws_kernel<0, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+  }
 #undef MLA_WS_ARGS
   return hipGetLastError();
 }

@@ -707,6 +707,25 @@ __device__ inline int quantize_q_quad(const i32x4 raw[16], uint2 codes[16]) {
   return e;
 }
 
+// gfx942's e4m3fnuz codes turned into OCP e4m3fn codes of the same value,
+// in place in this wave's 4 KiB slice of a landed tile (the fp8 matrix cores
+// read OCP codes only). A code whose exponent field is 2 or more is the OCP
+// code 8 lower (one less exponent: bias 8 against 7, same mantissa). The 16
+// smallest magnitudes (exponent field 0 or 1: multiples k 2^-10 of the scale,
+// k = 0 .. 15) become OCP subnormals, multiples of 2^-9, rounded to nearest
+// even: odd k moves by 2^-10 of the scale, k = 15 becomes the smallest OCP
+// normal. 0x80, fnuz's NaN, becomes 0x80 (-0). Four bytes per 32-bit lane
+// word, no byte carries into the next.
+__device__ inline unsigned fnuz4_to_ocp4(unsigned x) {
+  const unsigned t = x & 0x7f7f7f7fu;                                  // magnitude codes
+  const unsigned big = ((t + 0x70707070u) & 0x80808080u) >> 7;          // 1 where t >= 16
+  const unsigned bm = big * 0xffu;                                      // 0xff where t >= 16
+  const unsigned rb = ((t | 0x80808080u) - 0x08080808u) & 0x7f7f7f7fu;  // t - 8
+  const unsigned hh = (t >> 1) & 0x7f7f7f7fu;                           // t / 2
+  const unsigned rs = hh + (t & hh & 0x01010101u);                      // t / 2 to nearest even
+  return (x & 0x80808080u) | (rb & bm) | (rs & ~bm);
+}
+
 // The role-split decode (mla_decode_ws.hip): fp8 dots, per-tensor scales,
 // dense, three or more 32-row blocks per key stream.
 bool decode_ws_eligible(const DecodeLaunch& d);

@@ -86,15 +86,18 @@ extern "C" {
 /* kv_dtype codes. The OCP e4m3fn encoding (or a uint8 view of it) is read
  * by both dot modes. gfx942's e4m3fnuz (bias 8, largest magnitude 240, NaN
  * only at 0x80; ROCm/aiter PR #6199, Technical details) is read with
- * MLA_DOT_BF16 and per-tensor scales only: its codes are decoded exactly to
- * bf16 in registers (0x80, the NaN code, reads as zero), while the fp8
- * matrix cores read OCP codes only (MLA_DOT_FP8 or per-token scales with an
- * fnuz cache is MLA_ERR_UNSUPPORTED). The other one-byte encodings are
- * refused rather than misread (ROCm/aiter PR #6199, the foreign-encoding
- * refusal commit). */
+ * per-tensor scales only. MLA_DOT_BF16 decodes its codes exactly to bf16 in
+ * registers. MLA_DOT_FP8 (dense only; sparse is MLA_ERR_UNSUPPORTED) turns
+ * each landed tile's codes into the e4m3fn codes of the same values for the
+ * OCP fp8 matrix cores: exact for every magnitude from 2^-6 to 240 (in units
+ * of the scale); the fnuz magnitudes below 2^-6 (steps of 2^-10) go to
+ * e4m3fn's (steps of 2^-9) by round to nearest even, moving by at most
+ * 2^-10. In both modes 0x80, the NaN code, reads as zero. Per-token scales
+ * with an fnuz cache are MLA_ERR_UNSUPPORTED. The other one-byte encodings are refused rather than
+ * misread (ROCm/aiter PR #6199, the foreign-encoding refusal commit). */
 #define MLA_KV_FP8_E4M3FN 0
 #define MLA_KV_UINT8 1          /* raw bytes, taken to be e4m3fn */
-#define MLA_KV_FP8_E4M3FNUZ 2   /* bf16 dots, per-tensor scales; else MLA_ERR_UNSUPPORTED */
+#define MLA_KV_FP8_E4M3FNUZ 2   /* per-tensor scales; fp8 dots dense only */
 #define MLA_KV_FP8_E5M2 3       /* refused: MLA_ERR_UNSUPPORTED */
 #define MLA_KV_INT8 4           /* refused: MLA_ERR_UNSUPPORTED */
 #define MLA_KV_BF16 5           /* refused: MLA_ERR_UNSUPPORTED */
@@ -269,6 +272,11 @@ MLA_API int32_t mla_fp8_debug_decode_variant(const mla_params* p, const void* q,
  * use: to f32 (out_f32, may be NULL) and to bf16 bits (out_bf16, may be NULL). */
 MLA_API int32_t mla_fp8_debug_decode_e4m3fn(const uint8_t* codes, float* out_f32,
                                             uint16_t* out_bf16, int32_t n, void* hip_stream);
+
+/* The fp8-dot path's transcoding of an e4m3fnuz cache byte to the e4m3fn
+ * code of the same value (rounded to nearest even below 2^-6, 0x80 to 0x80;
+ * see the kv_dtype codes) on n bytes. */
+MLA_API int32_t mla_fp8_debug_fnuz_to_e4m3fn(const uint8_t* codes, uint8_t* out, int32_t n, void* hip_stream);
 
 /* Runs the fp8-dot path's query quantization on `rows` bf16 rows of length
  * row_len (the first 512 entries of each row are quantized): writes 512 codes

@@ -112,6 +112,26 @@ def decode_kv_codes(codes, encoding="e4m3fn") -> np.ndarray:
     raise ValueError(f"unknown encoding {encoding!r}")
 
 
+def fnuz_as_e4m3fn(codes) -> np.ndarray:
+    """e4m3fnuz bytes -> the e4m3fn bytes of the same values, for fp8 matrix
+    cores that read OCP codes only (ROCm/aiter PR #6199, Technical details:
+    gfx942's fnuz against gfx950's OCP e4m3).
+
+    Each fnuz value is encoded as e4m3fn by round to nearest, ties to even
+    (``encode_e4m3fn``). Every fnuz magnitude from 2**-6 up to 240 is an
+    e4m3fn value (e4m3fn reaches 448), so those codes keep their value
+    exactly; below 2**-6 fnuz steps by 2**-10 and e4m3fn by 2**-9, so half of
+    those 15 magnitudes round. 0x80, fnuz's NaN, is taken as zero (-0, 0x80),
+    as the decode reads it.
+    """
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        c = c.astype(np.uint8)
+    v = decode_e4m3fnuz(c)
+    v = np.where(c == 0x80, -0.0, v)
+    return encode_e4m3fn(v)
+
+
 def encode_e4m3fn(x) -> np.ndarray:
     """float64 -> e4m3fn bytes: round to nearest, ties to even, saturating.
 

@@ -30,7 +30,7 @@ def _declared_symbols():
 
 def test_every_declared_symbol_is_exported(L):
     names = _declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
     exported = set(re.findall(r"\bT (mla_fp8_\w+)", out))
     assert set(names) <= exported
@@ -52,7 +52,9 @@ def good(**kw):
 @pytest.mark.parametrize("kw,status", [
     ({}, mla.MLA_OK),
     ({"kv_dtype": torch.float8_e4m3fn}, mla.MLA_OK),
-    ({"kv_dtype": torch.float8_e4m3fnuz}, mla.MLA_ERR_UNSUPPORTED),            # fp8 dots (the default)
+    ({"kv_dtype": torch.float8_e4m3fnuz}, mla.MLA_OK),                         # fp8 dots (the default), dense
+    ({"kv_dtype": torch.float8_e4m3fnuz, "topk": 8, "d_rope": 0}, mla.MLA_ERR_UNSUPPORTED),   # fp8 dots, sparse
+    ({"kv_dtype": torch.float8_e4m3fnuz, "per_token_scales": True}, mla.MLA_ERR_UNSUPPORTED),
     ({"kv_dtype": torch.float8_e4m3fnuz, "dot": "bf16"}, mla.MLA_OK),           # decoded to bf16 in registers
     ({"kv_dtype": torch.float8_e4m3fnuz, "dot": "bf16", "per_token_scales": True}, mla.MLA_ERR_UNSUPPORTED),
     ({"kv_dtype": torch.float8_e5m2}, mla.MLA_ERR_UNSUPPORTED),
@@ -181,9 +183,15 @@ def test_decode_variant_rejects_unknown_bits_before_any_launch(L):
     bad = good(h_kv=2)
     args[0] = ctypes.byref(bad)
     assert L.mla_fp8_debug_decode_variant(*args, mla.MLA_VARIANT_ROWS, None) == mla.MLA_ERR_UNSUPPORTED
+    # an fnuz cache with fp8 dots has no variant kernels
+    fz = good(kv_dtype=torch.float8_e4m3fnuz)
+    args[0] = ctypes.byref(fz)
+    assert L.mla_fp8_debug_decode_variant(*args, mla.MLA_VARIANT_ROWS, None) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_debug_exports_check_arguments(L):
+    assert L.mla_fp8_debug_fnuz_to_e4m3fn(None, ctypes.c_void_p(16), 4, None) == mla.MLA_ERR_NULL
+    assert L.mla_fp8_debug_fnuz_to_e4m3fn(ctypes.c_void_p(16), ctypes.c_void_p(16), -1, None) == mla.MLA_ERR_SHAPE
     assert L.mla_fp8_debug_decode_e4m3fn(None, None, None, 4, None) == mla.MLA_ERR_NULL
     assert L.mla_fp8_debug_quantize_q(ctypes.c_void_p(16), 1, 100, ctypes.c_void_p(16), ctypes.c_void_p(16),
                                       None) == mla.MLA_ERR_SHAPE

@@ -5,9 +5,14 @@ value, ROCm/aiter PR #6199, Technical details); the oracle decodes them from
 the fnuz bit fields. Each workload's amax element carries the +-240 codes
 (0x7F / 0xFF, NaN in e4m3fn), and the unowned rows hold 0x80, fnuz's NaN.
 
-The bf16-dot path reads the cache; every case checks that the kernel reads
-the +-240 codes as 240. 0x80, fnuz's NaN, reads as zero. fp8 dots refuse an
-fnuz cache (host check, no launch).
+The bf16-dot path reads the cache exactly; every case checks that the kernel
+reads the +-240 codes as 240. 0x80, fnuz's NaN, reads as zero in both modes.
+The fp8-dot path (dense) turns each landed tile's codes into the e4m3fn codes
+of the same values (oracle.fp8.fnuz_as_e4m3fn, checked here bit for bit on
+all 256 codes): exact from 2^-6 of the scale up to 240, rounded to nearest
+even below. Its cases are held to the fp8 tolerances both against the oracle
+reading the fnuz cache exactly and against the oracle on the transcoded
+cache. Sparse fp8 dots refuse an fnuz cache (host check, no launch).
 """
 
 import numpy as np
@@ -70,9 +75,60 @@ def test_fnuz_nan_code_reads_as_zero():
     gu.compare(out, lse, ref_o, ref_l, dot="bf16")
 
 
-def test_fnuz_cache_is_refused_with_fp8_dots():
-    w = workloads.make("tiny", batch=2, s_q=2, h_q=16, seq_len=[100, 80], encoding="e4m3fnuz", seed=126)
+def _transcoded(w):
+    """The workload with its nope bytes replaced by the e4m3fn codes the fp8-dot
+    path reads (oracle.fp8.fnuz_as_e4m3fn), as an e4m3fn cache."""
+    import copy
+    from oracle import fp8
+    w2 = copy.copy(w)
+    kv = w.kv_cache.copy()
+    kv[..., :w.d_nope] = fp8.fnuz_as_e4m3fn(kv[..., :w.d_nope])
+    w2.kv_cache = kv
+    w2.encoding = "e4m3fn"
+    return w2
+
+
+def test_fnuz_transcoding_is_bit_exact():
+    from oracle import fp8
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).repeat(3)[:763].to("cuda:0")   # ragged tail
+    out = mla.debug_fnuz_to_e4m3fn(codes).cpu().numpy()
+    assert np.array_equal(out, fp8.fnuz_as_e4m3fn(codes.cpu().numpy()))
+
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+@pytest.mark.parametrize("idx", range(3))
+def test_fnuz_parity_fp8_dots(idx, splits):
+    name, kw = CASES[idx]
+    w, oc, t = _case(name, **kw)
+    assert t["kv"].dtype == torch.float8_e4m3fnuz and _has_top_codes(w)
+    res = gu.check(w, oc, "fp8", num_splits=splits, t=t)
+    # against the oracle on the cache as the fp8 path reads it
+    out, lse = gu.run(w, t, "fp8", num_splits=splits)
+    oc2 = gu.OracleCache(_transcoded(w))
+    res2 = gu.compare(out, lse, *oc2.exact, oc2.qprime[1], "fp8", ref_out_rows=oc2.qprime[0])
+    print(f"fnuz fp8 dots {name}{kw} splits={splits}: vs exact fnuz {res}; vs the transcoded cache {res2}")
+
+
+def test_fnuz_full_benchmark_shape_fp8_dots():
+    w, oc, t = _case("metric")
+    res = gu.check(w, oc, "fp8", t=t)
+    print(f"fnuz metric fp8 dots: {res}")
+
+
+def test_fnuz_nan_code_reads_as_zero_fp8_dots():
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=16, seq_len=[100, 80], encoding="e4m3fnuz", seed=127)
+    page = int(w.block_table[0, 0])
+    w.kv_cache[page, 5, 17] = 0x80
     t = gu.device_inputs(w)
+    out, lse = gu.run(w, t, "fp8", num_splits=1)
+    w.kv_cache[page, 5, 17] = 0x00
+    oc = gu.OracleCache(_transcoded(w))
+    gu.compare(out, lse, *oc.exact, oc.qprime[1], "fp8", ref_out_rows=oc.qprime[0])
+
+
+def test_fnuz_cache_is_refused_with_sparse_fp8_dots():
+    name, kw = CASES[3]
+    w, oc, t = _case(name, **kw)
     assert t["kv"].dtype == torch.float8_e4m3fnuz
     with pytest.raises(mla.MlaError) as e:
         gu.run(w, t, "fp8", num_splits=1)

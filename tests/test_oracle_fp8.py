@@ -160,3 +160,43 @@ def test_kv_code_dispatch():
     assert np.array_equal(fp8.decode_kv_codes(c, "e4m3fnuz"), fp8.E4M3FNUZ_TABLE, equal_nan=True)
     with pytest.raises(ValueError):
         fp8.decode_kv_codes(c, "e5m2")
+
+
+def test_fnuz_as_e4m3fn_keeps_values_from_2_pow_minus_6_up():
+    # every fnuz magnitude in [2**-6, 240] is an e4m3fn value: the transcoding
+    # keeps it; 240 (0x7F) is e4m3fn 0x77, one exponent lower in the code
+    codes = np.arange(256, dtype=np.uint8)
+    out = fp8.fnuz_as_e4m3fn(codes)
+    v_in = fp8.decode_e4m3fnuz(codes)
+    v_out = fp8.decode_e4m3fn(out)
+    big = (codes & 0x7F) >= 0x10
+    assert np.array_equal(v_out[big], v_in[big])
+    assert out[0x7F] == 0x77 and out[0xFF] == 0xF7 and fp8.decode_e4m3fn(np.uint8(0x77)) == 240.0
+    # and the code is the fnuz code 8 lower (bias 8 against 7, same mantissa)
+    assert np.array_equal(out[big], codes[big] - 8)
+
+
+def test_fnuz_as_e4m3fn_rounds_the_smallest_magnitudes_to_even():
+    # fnuz exponent field 0 or 1: k * 2**-10 (k = 0..15); e4m3fn subnormals are
+    # m * 2**-9, then 2**-6: k rounds to 2 m with ties to the even mantissa
+    for k in range(16):
+        out = int(fp8.fnuz_as_e4m3fn(np.uint8(k)))
+        exact = k * 2.0 ** -10
+        got = float(fp8.decode_e4m3fn(np.uint8(out)))
+        assert abs(got - exact) <= 2.0 ** -10
+        if k % 2 == 0:
+            assert got == exact
+        else:
+            assert (out & 1) == 0, (k, out)     # the tie went to the even code
+    assert fp8.fnuz_as_e4m3fn(np.uint8(15)) == 0x08      # 15 * 2**-10 -> 2**-6, the smallest normal
+    assert fp8.fnuz_as_e4m3fn(np.uint8(0x89)) == 0x84    # sign kept: -9 * 2**-10 -> -4 * 2**-9
+    assert fp8.fnuz_as_e4m3fn(np.uint8(0x80)) == 0x80    # fnuz NaN read as zero
+
+
+def test_fnuz_as_e4m3fn_against_torch_casts():
+    # an outside check: torch's fnuz decode, then torch's e4m3fn cast (RNE)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fnuz).to(torch.float32)
+    vals = torch.where(torch.isnan(vals), torch.tensor(-0.0), vals)
+    ref = vals.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.fnuz_as_e4m3fn(np.arange(256, dtype=np.uint8)), ref)
