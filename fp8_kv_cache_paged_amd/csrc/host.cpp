@@ -52,7 +52,11 @@ int32_t validate(const mla_params* p) {
     default:
       return MLA_ERR_DTYPE;
   }
-  if (p->batch < 1 || p->s_q < 1 || p->s_q > 1024 || p->h_q < 1 || p->h_q > 1024) return MLA_ERR_SHAPE;
+  // dense rows share a key stream per sequence (s_q * h_q of them); sparse
+  // query tokens each carry their own index list, so a long prefill is many
+  // independent groups
+  if (p->batch < 1 || p->s_q < 1 || p->s_q > (p->topk > 0 ? 65536 : 1024) || p->h_q < 1 || p->h_q > 1024)
+    return MLA_ERR_SHAPE;
   if (p->num_pages < 1 || p->max_pages_per_seq < 1 || p->topk < 0) return MLA_ERR_SHAPE;
   if (p->causal != 0 && p->causal != 1) return MLA_ERR_SHAPE;
   if (p->kv_scale_per_token != 0 && p->kv_scale_per_token != 1) return MLA_ERR_SHAPE;

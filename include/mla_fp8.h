@@ -111,9 +111,12 @@ extern "C" {
 /* Host-side description of the tensors. */
 typedef struct mla_params {
   int32_t batch;              /* sequences, >= 1 */
-  int32_t s_q;                /* query tokens per sequence, 1..1024 (2 with MTP; up to
-                                 16 for multi-token decode, more for a causal
-                                 prefill chunk: the last s_q tokens of the sequence) */
+  int32_t s_q;                /* query tokens per sequence: 1..1024 dense (2 with MTP;
+                                 up to 16 for multi-token decode, more for a causal
+                                 prefill chunk: the last s_q tokens of the sequence);
+                                 1..65536 sparse, where every token carries its own
+                                 index list (a sparse prefill, ROCm/aiter PR #6199,
+                                 Results: 16K tokens) */
   int32_t h_q;                /* query heads, 1..1024 */
   int32_t h_kv;               /* latent KV heads: must be 1 */
   int32_t d_nope;             /* must be 512 */

@@ -174,3 +174,34 @@ def test_dv_split_kernel_matches_row_block_kernel(case):
         a = gu.run(w, t, "fp8", splits, variant=mla.MLA_VARIANT_DV_SPLIT)
         b = gu.run(w, t, "fp8", splits, variant=mla.MLA_VARIANT_ROWS)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"splits={splits}"
+
+
+# ---- the 16K-token sparse prefill (ROCm/aiter PR #6199, Results) -------------------
+# Full size on the GPU; the oracle on a sample of 384 tokens spread over the
+# 16K (sparse tokens are independent: each its own index list, no causal mask).
+
+_SP = {}
+
+
+def _sparse_prefill():
+    if not _SP:
+        w = workloads.make("sparse_prefill")
+        _SP["w"], _SP["t"] = w, gu.device_inputs(w)
+    return _SP["w"], _SP["t"]
+
+
+@pytest.mark.parametrize("dot", ["fp8", "bf16"])
+def test_sparse_prefill_16k_tokens(dot):
+    import copy
+    w, t = _sparse_prefill()
+    assert w.s_q == 16384 and w.topk == 2048
+    out, lse = gu.run(w, t, dot)
+    tok = np.arange(7, w.s_q, w.s_q // 384)[:384]
+    ws = copy.copy(w)
+    ws.s_q = len(tok)
+    ws.q_bits = w.q_bits[:, tok]
+    ws.indices = w.indices[:, tok]
+    oc = gu.OracleCache(ws)
+    ref_q = oc.qprime if dot == "fp8" else oc.exact
+    res = gu.compare(out[:, tok], lse[:, tok], *oc.exact, ref_q[1], dot, ref_out_rows=ref_q[0])
+    print(f"sparse prefill 16K, {dot} dots, {len(tok)} sampled tokens: {res}")

@@ -71,9 +71,14 @@ SPECS = {
     # sequences attend causally to the whole cache (16 heads)
     "prefill": dict(batch=2, s_q=256, h_q=16, d_rope=64, seq_len=4096, causal=True,
                     num_splits=0, dots=("bf16", "fp8")),
+    # sparse prefill (the aiter PR's third workload, same model shard): 16K
+    # query tokens of one sequence, each with its own top-2048 of the 16K keys
+    "sparse_prefill": dict(batch=1, s_q=16384, h_q=16, d_rope=0, seq_len=16384, causal=False,
+                           topk=2048, peaky=True, num_splits=0, dots=("bf16", "fp8")),
 }
 
-SEEDS = {"tiny": 1, "mtp": 2, "varlen": 3, "large": 4, "sparse": 5, "metric": 6, "sparse16": 7, "prefill": 8}
+SEEDS = {"tiny": 1, "mtp": 2, "varlen": 3, "large": 4, "sparse": 5, "metric": 6, "sparse16": 7, "prefill": 8,
+         "sparse_prefill": 9}
 
 
 @dataclass
