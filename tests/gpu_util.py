@@ -82,6 +82,22 @@ class OracleCache:
         return oracle(self.w, q_prime=True)
 
 
+def page_metrics(x, y, name):
+    """The accuracy figures of FlashMLA PR #82's H800 test report (out and lse:
+    cos_diff, RMSE, amax_diff), read as: cos_diff = 1 - cosine similarity of
+    the flattened tensors, RMSE = root mean square of x - y, amax_diff =
+    max |x - y|, all in float64 (the page names them without a formula)."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    y = np.asarray(y, dtype=np.float64).ravel()
+    if x.size == 0:
+        return {}
+    nx, ny = np.linalg.norm(x), np.linalg.norm(y)
+    cos = float(np.dot(x, y) / (nx * ny)) if nx > 0 and ny > 0 else 1.0
+    d = x - y
+    return {f"{name}_cos_diff": 1.0 - cos, f"{name}_rmse": float(np.sqrt(np.mean(d * d))),
+            f"{name}_amax_diff": float(np.max(np.abs(d)))}
+
+
 def compare(out, lse, ref_out, ref_lse, ref_lse_for_lse=None, dot="fp8", ref_out_rows=None):
     """Returns a dict of error figures and asserts the tolerances. ref_out,
     ref_lse: the oracle at the bf16 query; ref_lse_for_lse and ref_out_rows:
@@ -104,6 +120,8 @@ def compare(out, lse, ref_out, ref_lse, ref_lse_for_lse=None, dot="fp8", ref_out
     row_rel = row_err / np.where(row_ref > 0, row_ref, 1.0)
     row_max = float(row_rel.max()) if row_rel.size else 0.0
     res = {"rel_l2": rel, "row_rel_l2_max": row_max, "lse_max_abs": dl, "lse_max_abs_vs_bf16q": dl_plain}
+    res.update(page_metrics(out[live], ref_out[live], "out"))
+    res.update(page_metrics(lse[live], ref_lse_l[live], "lse"))
     assert rel <= OUT_TOL[dot], f"rel-L2 {rel:.3e} > {OUT_TOL[dot]} ({dot} dots)"
     assert row_max <= ROW_TOL[dot], f"worst row rel-L2 {row_max:.3e} > {ROW_TOL[dot]} ({dot} dots)"
     assert dl <= LSE_TOL, f"max |dlse| {dl:.3e} > {LSE_TOL}"

@@ -205,3 +205,27 @@ def test_sparse_prefill_16k_tokens(dot):
     ref_q = oc.qprime if dot == "fp8" else oc.exact
     res = gu.compare(out[:, tok], lse[:, tok], *oc.exact, ref_q[1], dot, ref_out_rows=ref_q[0])
     print(f"sparse prefill 16K, {dot} dots, {len(tok)} sampled tokens: {res}")
+
+
+# ---- FlashMLA PR #82's H800 accuracy report, at its shape -----------------------
+# b=64, s_q=2, mean_sk=4096, h_q=64, causal, fp8 cache: the "varlen" workload
+# (seq lens U{2048..6144}). The page's figures (another machine, another
+# implementation) are context; printed beside ours for the report.
+
+PAGE_H800 = {"out_cos_diff": 6.64e-4, "out_rmse": 1.78e-3, "out_amax_diff": 4.80e-2,
+             "lse_cos_diff": 3.26e-11, "lse_rmse": 7.12e-5, "lse_amax_diff": 2.16e-4}
+
+
+@pytest.mark.parametrize("dot", ["fp8", "bf16"])
+def test_accuracy_report_at_the_h800_shape(dot):
+    w, oc, t = _case("varlen")
+    assert w.batch == 64 and w.s_q == 2 and w.h_q == 64 and 2048 <= w.seq_lens.min() and w.seq_lens.max() <= 6144
+    out, lse = gu.run(w, t, dot)
+    ref_o, ref_l = oc.exact                      # the plain oracle (bf16 query) for both tensors
+    live = ~np.isneginf(ref_l)
+    m = {}
+    m.update(gu.page_metrics(out[live], ref_o[live], "out"))
+    m.update(gu.page_metrics(lse[live], ref_l[live], "lse"))
+    print(f"H800-shape accuracy, {dot} dots: " + ", ".join(f"{k} {v:.3g} (page {PAGE_H800[k]:.3g})"
+                                                          for k, v in m.items()))
+    assert m["out_cos_diff"] < 1e-2 and m["lse_cos_diff"] < 1e-6
