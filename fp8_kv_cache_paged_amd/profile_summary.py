@@ -14,8 +14,8 @@ The HBM traffic of the split kernel is the per-dispatch counter value scaled
 by what the same counter reads for kernels of known size in the same run: the
 2 GiB streaming read that bench.py times (FETCH_SIZE) and torch's 2 GiB fill
 before it (WRITE_SIZE). The report records the SHA-256 of the kernel source it
-was taken with; bench.py only reports the traffic while the source is
-unchanged.
+was taken with (mla_decode_ws.hip, mla_decode.hip, mla_device.h); bench.py
+only reports the traffic while those are unchanged.
 
 ``--per-config NAME=DIR ... --out FILE`` instead summarizes one
 ``--kernel-trace --stats`` run per workload: the average duration of the
@@ -32,15 +32,19 @@ import json
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(PKG, "csrc", "mla_decode.hip")
-SPLIT_KERNEL = "mla::mla_decode_kernel<"
+# the decode kernels' sources: the report is valid while they are unchanged
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mla_decode_ws.hip", "mla_decode.hip", "mla_device.h")]
+SPLIT_KERNEL = "mla::mla_decode_ws_kernel<"   # the benchmark shape's split kernel (fp8 dots)
 STREAM_BYTES = 2 << 30          # bench.py's HBM read probe
 FILL_BYTES = 2 << 30            # torch fill of the same buffer
 
 
-def source_sha256(path=KERNEL_SOURCE):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha256(paths=None):
+    h = hashlib.sha256()
+    for path in paths or KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _one(pattern):
@@ -157,7 +161,7 @@ def main():
         return
     st = kernel_stats(a.stats)
     tr = traffic(a.fetch, a.write)
-    lines = ["# rocprofv3 summary: mla_decode_kernel (fp8 dots), benchmark workload", ""]
+    lines = ["# rocprofv3 summary: mla_decode_ws_kernel (fp8 dots), benchmark workload", ""]
     lines += ["commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):"]
     lines += [f"  {c}" for c in a.command]
     lines += ["", f"source_sha256: {source_sha256()}", ""]
