@@ -91,7 +91,7 @@ int32_t resolve(const mla_params& p, int32_t num_splits, int32_t cu_count) {
 
 size_t workspace(const mla_params& p, int32_t splits) {
   if (splits <= 1) return 0;
-  return mla::partials_bytes(splits, groups_of(p), (rows_of(p) + 31) / 32);
+  return mla::partials_bytes(splits, groups_of(p), (rows_of(p) + 31) / 32, p.kv_scale_per_token != 0);
 }
 
 std::mutex g_cu_mutex;

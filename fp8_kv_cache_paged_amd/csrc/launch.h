@@ -51,7 +51,10 @@ struct DecodeLaunch {
 };
 
 // Bytes of the partial-output workspace for the given geometry.
-size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks);
+// Split partials: fp16 values in the accumulator layout, then an f32 log2-lse
+// per row, then (per-token scales only) an f32 scale per row that multiplies
+// the row's stored values (part_row_scale).
+size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks, bool per_token);
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 hipError_t launch_combine(const DecodeLaunch& d, hipStream_t stream);

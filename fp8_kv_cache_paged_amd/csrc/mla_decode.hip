@@ -512,8 +512,25 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   const bool nonempty = l_tot > 0.f;
   // splits == 1: the output, scaled by v_scale; else the partials, normalized
   // by the row sum only (fp16, |value| <= 448; the combine applies v_scale)
-  // (fnuz: V decoded to 2^-119 times its value, restored here)
-  const float inv = nonempty ? ldexpf(PT ? 1.f : (a.splits == 1 ? *v_scale : 1.f), FNUZ ? kFnuzExp : 0) / l_tot : 0.f;
+  // (fnuz: V decoded to 2^-119 times its value, restored here). Per-token
+  // scales: O carries the scales already; partials are stored over a power of
+  // two near the row's largest value (|value| <= 1), kept beside the lse.
+  float inv = nonempty ? ldexpf(PT ? 1.f : (a.splits == 1 ? *v_scale : 1.f), FNUZ ? kFnuzExp : 0) / l_tot : 0.f;
+  float row_scale = 1.f;
+  if (PT && a.splits > 1) {
+    float mx = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 16; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(O[blk][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * inv;
+    if (mx > 0.f && mx <= 3.0e38f) {
+      int e;
+      frexpf(mx, &e);             // mx = f * 2^e, 0.5 <= f < 1
+      row_scale = ldexpf(1.f, e);
+      inv = ldexpf(inv, -e);
+    }
+  }
   const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
 
   if (a.splits == 1) {
@@ -547,7 +564,10 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         dst[j] = w;
       }
     }
-    if (h == 0) part_lse[frag * 32 + n] = lse2;
+    if (h == 0) {
+      part_lse[frag * 32 + n] = lse2;
+      if (PT) part_row_scale(part_lse, a)[frag * 32 + n] = row_scale;
+    }
   }
 }
 
@@ -1106,15 +1126,19 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
                  "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const bool nonempty = l_tot > 0.f;
-  // splits == 1: output scale v_scale / l; else the partials' 1 / l (fp16
-  // partials, |value| <= 448; the combine applies v_scale)
-  if (h == 0) xfin[wave * 32 + n] = nonempty ? (PT ? vref : (a.splits == 1 ? *v_scale : 1.f)) / l_tot : 0.f;
+  // splits == 1: output scale (v_scale or, per token, V_ref) / l; else the
+  // partials' 1 / l (fp16 partials in code units, |value| <= 448; the combine
+  // applies v_scale, or the per-row V_ref stored beside the lse)
+  if (h == 0)
+    xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? (PT ? vref : *v_scale) : 1.f) / l_tot : 0.f;
   if (wave_active && h == 0) {
     const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT>::ps_log2 : -INFINITY;
     if (a.splits == 1) {
       if (row_ok) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
     } else {
-      part_lse[(((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n] = lse2;
+      const long prow = (((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n;
+      part_lse[prow] = lse2;
+      if (PT) part_row_scale(part_lse, a)[prow] = vref;
     }
   }
   __syncthreads();
@@ -1186,19 +1210,22 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims
   float acc[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const float* const pscale = a.per_token ? part_row_scale(part_lse, a) : nullptr;
   for (int s0 = 0; s0 < a.splits; s0 += 4) {
-    float ls[4];
+    float ls[4], sc[4];
     i32x4 v0[4], v1[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (s0 + u < a.splits) {
         const long frag = frag0 + (s0 + u) * fstride;
         ls[u] = part_lse[frag * 32 + n];
+        sc[u] = pscale != nullptr ? pscale[frag * 32 + n] : 1.f;
         const i32x4* src = reinterpret_cast<const i32x4*>(part_o + frag * (16 * 64 * 16) + (blk * 64 + lane) * 16);
         v0[u] = src[0];
         v1[u] = src[1];
       } else {
         ls[u] = -INFINITY;
+        sc[u] = 0.f;
         v0[u] = v1[u] = i32x4{0, 0, 0, 0};
       }
     }
@@ -1210,8 +1237,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims
     for (int r = 0; r < 16; ++r) acc[r] *= alpha;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float w = exp2f(ls[u] - m_new);   // 0 for an empty split
-      W += w;
+      const float w0 = exp2f(ls[u] - m_new);   // 0 for an empty split
+      W += w0;
+      const float w = w0 * sc[u];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         acc[2 * d] += w * half_lo((unsigned)v0[u][d]);
@@ -1222,7 +1250,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims
     }
     M = m_new;
   }
-  const float inv = W > 0.f ? (a.per_token ? 1.f : *v_scale) / W : 0.f;   // per token: in the partials
+  const float inv = W > 0.f ? (a.per_token ? 1.f : *v_scale) / W : 0.f;   // per token: the row scales
   const long qrow_idx = (long)g * a.rows + row;
   uint16_t* orow = out + qrow_idx * kNope;
 #pragma unroll
@@ -1366,9 +1394,9 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const i32x4* src, long
 // ---------------------------------------------------------------------------
 // host-side launchers
 
-size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks) {
+size_t partials_bytes(int32_t splits, int32_t groups, int32_t row_blocks, bool per_token) {
   const size_t frags = (size_t)splits * groups * row_blocks;
-  return frags * (16 * 64 * 16 * sizeof(uint16_t)) + frags * 32 * sizeof(float);
+  return frags * (16 * 64 * 16 * sizeof(uint16_t)) + frags * 32 * sizeof(float) * (per_token ? 2 : 1);
 }
 
 // Waves per workgroup: one per 32-row block, up to 4 (1, 2 or 4 so that the

@@ -609,6 +609,14 @@ struct KDims {
   int32_t per_token;  // k_scale, v_scale hold one value per cache row
 };
 
+// Per-token scales, splits > 1: the f32 factor per partial row that follows
+// the log2-lse array; the row's stored fp16 values times it are the split's
+// normalized output. It keeps the stored values within fp16's range and away
+// from its subnormals whatever the magnitude of the scales.
+__device__ inline float* part_row_scale(float* part_lse, const KDims& a) {
+  return part_lse + (long)a.splits * a.groups * a.row_blocks * 32;
+}
+
 #define MLA_KERNEL_PTRS                                                                   \
   const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,                         \
       const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,      \

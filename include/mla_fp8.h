@@ -159,7 +159,9 @@ MLA_API int32_t mla_fp8_decode_resolve_splits(const mla_params* p, int32_t num_s
  * grows from zero to splits x sequences x heads x (value size + 2) floats,
  * the workspace holds one partial per split and query row: here the 512
  * partial output values in fp16 and one f32 log-sum-exp, padded to 32-row
- * blocks: splits * groups * ceil(rows / 32) * (32 KiB + 128 B). The caller
+ * blocks: splits * groups * ceil(rows / 32) * (32 KiB + 128 B); with per-token
+ * scales also one f32 per row that scales its stored values (+128 B per
+ * block; the values stay within fp16's normal range at any scale). The caller
  * owns it; its contents need no initialization and are overwritten by every
  * call. Returns 0 for invalid *p or splits < 1. Host-only, no HIP call. */
 MLA_API size_t mla_fp8_decode_workspace_size(const mla_params* p, int32_t splits);

@@ -131,6 +131,9 @@ def test_workspace_size(L):
     q = good(batch=3, s_q=1, h_q=16)                  # one row block per sequence
     assert mla.workspace_size(q, 2) == 2 * 3 * (16 * 64 * 16 * 2 + 32 * 4)
     assert mla.workspace_size(good(batch=0), 4) == 0
+    # per-token scales: one more f32 per partial row (its value scale)
+    pt = good(batch=64, s_q=2, h_q=64, per_token_scales=True)
+    assert mla.workspace_size(pt, 4) == frags * (16 * 64 * 16 * 2 + 2 * 32 * 4)
 
 
 def _decode_call(L, p, **ptrs):

@@ -80,6 +80,22 @@ def test_per_token_decode_matches_oracle(name, kw, splits, dot):
     print(f"per-token {dot} {kw} splits={splits}: {res}")
 
 
+@pytest.mark.parametrize("factor", [1e-4, 1e4, 1e6])
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("dot", ["fp8", "bf16"])
+def test_per_token_decode_at_extreme_value_scales(factor, splits, dot):
+    """The v-scales far from 1: the output is factor times the unscaled one,
+    so every relative error must stay where it is. Split partials hold values
+    over a per-row scale, which keeps them inside fp16's normal range (at
+    1e-4 the values are ~1e-5, fp16 subnormals if stored as they are; at 1e6
+    they pass fp16's largest value)."""
+    w = workloads.make("tiny", batch=2, s_q=2, h_q=64, seq_len=[700, 190], seed=131)
+    ks, vs = _scales(w, 131)
+    vs = (vs.astype(np.float64) * factor).astype(np.float32)
+    res = _check(w, ks, vs, splits, dot)
+    print(f"per-token {dot} v-scales x{factor:g} splits={splits}: {res}")
+
+
 @pytest.mark.parametrize("dot", ["fp8", "bf16"])
 def test_per_token_decode_sparse_configuration(dot):
     w = workloads.make("sparse")
