@@ -444,6 +444,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         const i32x8 cur = vr[blk % PDV];
         if (blk + PDV < 16) vr[blk % PDV] = vfrag(blk + PDV);
         if (blk == 0) mfma_fp8_32x32x64_acc_after_valu(O[blk], cur, pb);   // pb was just written by VALU
+        else if (blk == 15) mfma_fp8_32x32x64_acc_last(O[blk], cur, pb);
         else mfma_fp8_32x32x64_acc(O[blk], cur, pb);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -481,7 +482,8 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
         for (int u = 0; u < 4; ++u) {
           const i32x2 lo = kv_bytes_to_bf16x4<FNUZ>(cur[2 * u]), hi = kv_bytes_to_bf16x4<FNUZ>(cur[2 * u + 1]);
           const bf16x8 av = __builtin_bit_cast(bf16x8, i32x4{lo.x, lo.y, hi.x, hi.y});
-          mfma_bf16_32x32x16_acc(O[blk], av, pb[u]);
+          if (blk == 15 && u == 3) mfma_bf16_32x32x16_acc_last(O[blk], av, pb[u]);
+          else mfma_bf16_32x32x16_acc(O[blk], av, pb[u]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -490,14 +492,6 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
     page_next = page_next2;
     row_cur = row_next;
     buf = buf_next;
-    if (k + 1 == ntiles) {
-      // the last P.V products finish before the loop is left (the compiler may
-      // copy the accumulators out at the exit, where it cannot see them busy)
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                   : "+a"(O[0]), "+a"(O[1]), "+a"(O[2]), "+a"(O[3]), "+a"(O[4]), "+a"(O[5]), "+a"(O[6]),
-                     "+a"(O[7]), "+a"(O[8]), "+a"(O[9]), "+a"(O[10]), "+a"(O[11]), "+a"(O[12]), "+a"(O[13]),
-                     "+a"(O[14]), "+a"(O[15]));
-    }
   }
 
   if (!wave_active) return;

@@ -576,6 +576,19 @@ __device__ inline void mfma_fp8_32x32x64_acc_after_valu(f32x16& acc, const i32x8
 __device__ inline void mfma_bf16_32x32x16_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// The last O^T products of a tile, followed by the wait states of their
+// results (passes + 4): whatever comes next, in the next iteration or after
+// the tile loop (where the compiler may copy the accumulators), sees them
+// complete. Only this product's accumulator is named, so the wait costs no
+// register constraint on the others.
+__device__ inline void mfma_fp8_32x32x64_acc_last(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_bf16_32x32x16_acc_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(acc) : "v"(a), "v"(b));
+}
 __device__ inline void s_nop_result(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }

@@ -65,8 +65,9 @@ CASES = [
 # The sparse workload is peaky: one key ~9 above the rest, whose tail holds a
 # fifth of the weight at p ~ e^-9 of the top key. With per-token scales, P is
 # multiplied by v_j / V_ref (<= 1) before its e4m3fn packing, which pushes
-# that tail further into the format's subnormal range: its scales here spread
-# 2x (the dense cases 8x).
+# that tail further into the format's subnormal range; the small sparse cases
+# spread the scales 2x, the full configuration is run at 2x and at the dense
+# cases' 8x.
 SPREAD = {"tiny": 8.0, "sparse": 2.0}
 
 
@@ -104,9 +105,6 @@ def test_per_token_decode_sparse_configuration(dot):
     print(f"per-token sparse {dot}: {res}")
 
 
-@pytest.mark.skip(reason="fp8 dots scale each p by v_j / V_ref (V_ref the split's largest v-scale) before "
-                         "the e4m3fn packing; at an 8x spread the peaky tail (p ~ 2^-13 of the top key) falls "
-                         "below e4m3fn's smallest subnormal and is flushed, so the case misses the bound")
 def test_per_token_decode_sparse_configuration_full_spread():
     w = workloads.make("sparse")
     ks, vs = _scales(w, 129, 8.0)
