@@ -158,7 +158,7 @@ def cpu_baseline(w, budget_s):
                       f"scaled: {sec_per_call:.2f} s per full call"}
 
 
-def main_quantize(args, dev, hbm_meas):
+def main_quantize(args, dev):
     """Quantize-on-write of the benchmark shape's whole cache in one call: 64
     sequences x 8196 tokens of bf16 latent (512) + rope (64) into shuffled
     64-token pages, the scale computed (amax / 448). Algorithmic bytes per
@@ -182,22 +182,32 @@ def main_quantize(args, dev, hbm_meas):
     L = mla.lib()
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    a = (n, 64, pages, vp(ckv), vp(rope), vp(slots), vp(kv), vp(ks), vp(vs), 1, vp(ws), ws.numel(), st)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        L.mla_fp8_quantize_kv(*a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        rc = L.mla_fp8_quantize_kv(*a)
-        if rc != 0:
-            raise RuntimeError(mla.status_string(rc))
-    e1.record(stream)
-    e1.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+
+    def timed(mode):
+        a = (n, 64, pages, vp(ckv), vp(rope), vp(slots), vp(kv), vp(ks), vp(vs), mode, vp(ws), ws.numel(), st)
+        for _ in range(args.warmup):
+            L.mla_fp8_quantize_kv(*a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            rc = L.mla_fp8_quantize_kv(*a)
+            if rc != 0:
+                raise RuntimeError(mla.status_string(rc))
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = timed(1)          # scale computed: the amax pass, then the encode pass
+    ms_given = timed(0)    # scale given: the encode pass alone
     nbytes = n * (1152 + 4 + 640)
+    # the amax pass reads every written row's 512 nope values (and its slot)
+    # again before the encode pass reads and writes them: 1.57x the
+    # algorithmic bytes when the scale is computed, 1.0x when it is given
+    moved = nbytes + n * (1024 + 4)
     gbps = nbytes / (ms * 1e-3) / 1e9
+    hbm_meas = hbm_read_probe(dev)   # after the timed regions, as for the decode
     line = {
         "metric": "FP8 KV quantize-on-write GB/s (64 x 8196 tokens, 576-wide latent)",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -205,6 +215,10 @@ def main_quantize(args, dev, hbm_meas):
         "dtype": "bf16->fp8", "data": "synthetic",
         "config": {"workload": f"quantize: {n} tokens, {pages} shuffled pages, scale computed"},
         "hbm_measured_gbps": round(hbm_meas, 1), "frac_of_measured_hbm": round(gbps / hbm_meas, 4),
+        "bytes_moved_per_call": moved, "moved_over_algorithmic": round(moved / nbytes, 3),
+        "given_scale": {"ms_per_step": round(ms_given, 5), "gbps": round(nbytes / (ms_given * 1e-3) / 1e9, 1),
+                        "frac_of_measured_hbm": round(nbytes / (ms_given * 1e-3) / 1e9 / hbm_meas, 4),
+                        "moved_over_algorithmic": 1.0},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "kv_amax_kernel + kv_encode_kernel", "bytes_per_launch": nbytes},
@@ -241,7 +255,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.op == "quantize":
-        return main_quantize(args, dev, hbm_read_probe(dev))
+        return main_quantize(args, dev)
 
     w = workloads.make(args.workload, encoding=args.kv_encoding)
     flops = workloads.flops(w)
@@ -345,8 +359,10 @@ def main():
     gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     mfma_peak = FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS
     if args.dot == "fp8":
-        ws_path = idx is None and not per_token and (w.s_q * w.h_q + 31) // 32 >= 3
-        kernel_name = "mla_decode_ws_kernel" if ws_path or args.kv_encoding == "e4m3fnuz" else "mla_decode_kernel"
+        # the role-split kernel: per-tensor scales, dense with >= 3 row blocks, any sparse shape, any fnuz
+        ws_path = not per_token and (idx is not None or (w.s_q * w.h_q + 31) // 32 >= 3
+                                     or args.kv_encoding == "e4m3fnuz")
+        kernel_name = "mla_decode_ws_kernel" if ws_path else "mla_decode_kernel"
     else:
         kernel_name = "mla_decode_kernel or mla_decode_rows_kernel"
     roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,

@@ -98,17 +98,13 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int32_t* idx_row = SPARSE ? indices + (long)g * a.topk : nullptr;
   constexpr long RB = kNope + 2 * ROPE;
 
-  // Cache row (page * 64 + slot) of sparse entry `e`, or -1 when skipped.
-  auto sparse_row = [&](int e) -> int {
-    int cr = -1;
-    if (e < a.topk) {
-      const int j = idx_row[e];
-      if (j >= 0 && j < sk) {
-        const int page = bt_row[j / kKeys];
-        if (page >= 0 && page < a.num_pages) cr = page * kKeys + (j % kKeys);
-      }
-    }
-    return cr;
+  // Sparse entry e's index, the page it falls in and its cache row (page * 64
+  // + slot, -1 when skipped): three steps, so that a pipeline can give each
+  // dependent load a whole tile iteration.
+  auto sparse_entry = [&](int e) -> int { return e < a.topk ? idx_row[e] : -1; };
+  auto sparse_page = [&](int j) -> int { return j >= 0 && j < sk ? bt_row[j / kKeys] : -1; };
+  auto sparse_cache_row = [&](int j, int page) -> int {
+    return j >= 0 && j < sk && page >= 0 && page < a.num_pages ? page * kKeys + (j % kKeys) : -1;
   };
   // Dense: one page per tile. Inside the tile loop page ids come from a
   // register holding 64 of them (lane i: tile 64c + i of the split), read with
@@ -141,9 +137,18 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   // computes); sparse tiles one ahead.
   int page_cur = -1, page_next = -1, page_next2 = -1;   // dense
   int row_cur = -1, row_next = -1;                      // sparse: this lane's tile row
+  // sparse: at the top of iteration k, j_b and pg_b are this lane's entry of
+  // tile k+1 and the page it falls in, j_c its entry of tile k+2 (each index
+  // and page-table load has a whole iteration to land)
+  int j_b = -1, pg_b = -1, j_c = -1;
   if (ntiles > 0) {
     if constexpr (SPARSE) {
-      row_cur = sparse_row(u0 * kKeys + lane);
+      const int j0 = sparse_entry(u0 * kKeys + lane);
+      if (ntiles > 1) j_b = sparse_entry((u0 + 1) * kKeys + lane);
+      if (ntiles > 2) j_c = sparse_entry((u0 + 2) * kKeys + lane);
+      const int pg0 = sparse_page(j0);
+      pg_b = sparse_page(j_b);
+      row_cur = sparse_cache_row(j0, pg0);
       issue_sparse_scales(row_cur, 0);
       issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
     } else {
@@ -215,9 +220,12 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
     const int buf_next2 = buf_next == kBufs - 1 ? 0 : buf_next + 1;
     if constexpr (SPARSE) {
       if (k + 1 < ntiles) {
-        row_next = sparse_row((u0 + k + 1) * kKeys + lane);
+        row_next = sparse_cache_row(j_b, pg_b);   // both landed by the wait above
         issue_sparse_scales(row_next, buf_next);
         issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
+        j_b = j_c;
+        pg_b = sparse_page(j_b);
+        j_c = k + 3 < ntiles ? sparse_entry((u0 + k + 3) * kKeys + lane) : -1;
       }
     } else {
       if (k + 2 < ntiles) {
@@ -671,6 +679,13 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     return cr;
   };
+  // The same in three steps, for a pipeline that gives each dependent load a
+  // whole tile iteration: the entry, the page it falls in, the cache row.
+  auto sparse_entry = [&](int e) -> int { return e < a.topk ? idx_row[e] : -1; };
+  auto sparse_page = [&](int j) -> int { return j >= 0 && j < sk ? bt_row[j / kKeys] : -1; };
+  auto sparse_cache_row = [&](int j, int page) -> int {
+    return j >= 0 && j < sk && page >= 0 && page < a.num_pages ? page * kKeys + (j % kKeys) : -1;
+  };
   // Dense: one page per tile. Inside the tile loop page ids come from a
   // register holding 64 of them (lane i: tile 64c + i of the split), read with
   // v_readlane: a scalar load there would share the counter of the LDS
@@ -709,9 +724,19 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
   // Tiles are loaded one ahead: tile k+1 lands while tile k computes.
   int page_cur = -1, page_next = -1;          // dense
   int row_cur = -1, row_next = -1;            // sparse: this lane's tile row
+  // sparse: at the top of iteration k, j_b and pg_b are this lane's entry of
+  // tile k+1 and the page it falls in, j_c its entry of tile k+2: every index
+  // and page-table load has a whole iteration to land, so the copies of tile
+  // k+1 go out without a dependent load in front of them
+  int j_b = -1, pg_b = -1, j_c = -1;
   if (ntiles > 0) {
     if constexpr (SPARSE) {
-      row_cur = sparse_row(u0 * kKeys + lane);
+      const int j0 = sparse_entry(u0 * kKeys + lane);
+      if (ntiles > 1) j_b = sparse_entry((u0 + 1) * kKeys + lane);
+      if (ntiles > 2) j_c = sparse_entry((u0 + 2) * kKeys + lane);
+      const int pg0 = sparse_page(j0);
+      pg_b = sparse_page(j_b);
+      row_cur = sparse_cache_row(j0, pg0);
       issue_sparse_scales(row_cur, 0);
       issue_sparse_tile<ROPE, NW>(lds, 0, kv, row_cur, lane, wave);
     } else {
@@ -825,9 +850,12 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
     auto t1u = [&](int t) { return u0 + t; };
     if (k + 1 < ntiles) {
       if constexpr (SPARSE) {
-        row_next = sparse_row((u0 + k + 1) * kKeys + lane);
+        row_next = sparse_cache_row(j_b, pg_b);   // both landed by the wait above
         issue_sparse_scales(row_next, buf_next);
         issue_sparse_tile<ROPE, NW>(lds, buf_next, kv, row_next, lane, wave);
+        j_b = j_c;
+        pg_b = sparse_page(j_b);
+        j_c = k + 3 < ntiles ? sparse_entry((u0 + k + 3) * kKeys + lane) : -1;
       } else {
         const int t1 = k + 1;
         if ((t1 & 63) == 0) {   // next 64 page ids (tile loops longer than 64 tiles)
@@ -1451,7 +1479,7 @@ static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t s
     }
   }
   if constexpr (DOT == DOT_FP8) {
-    if (!SPARSE && decode_ws_eligible(d)) return launch_decode_ws(d, a, st);
+    if (decode_ws_eligible(d)) return launch_decode_ws(d, a, st);
     if (d.rows_kernel) return launch_nw<DOT, ROPE, SPARSE, false, false>(d, a, st);
     return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, true>(d, a, st)
                       : launch_nw<DOT, ROPE, SPARSE, false, true>(d, a, st);

@@ -156,6 +156,64 @@ __device__ __attribute__((always_inline)) inline void ws_issue_rope(uint8_t* lds
   }
 }
 
+// Sparse path (top-k index lists): the cache rows of a tile's 64 entries are
+// found through two dependent loads, the entry's index and the page-table
+// slot it falls in. One wave brings both into LDS slots by 4-byte DMA copies,
+// each one iteration ahead of its use: the index of tile t+4 and the page of
+// tile t+3 while the waves work on tile t, so that the copies of tile t+2 and
+// the masks of tile t read only LDS. Lanes with no source (entries past the
+// list, skipped or out-of-range indices) copy from kWsMinusOne, so that every
+// copy instruction runs on all lanes and the copy counts per tile stay fixed.
+constexpr int kSpSlots = 5;            // index of tile t written at t-4, last read at t
+constexpr int kSpSlotBytes = 512;      // 64 indices, then 64 page ids
+__device__ __align__(16) const int32_t kWsMinusOne[64] = {
+    -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
+    -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
+    -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+// 16 zero bytes per lane: the source of a skipped entry's tile bytes (a
+// masked key's P is 0, and 0 times a finite code is 0).
+__device__ __align__(16) const uint8_t kWsZeros[64 * 16] = {};
+
+// Cache row (page * 64 + slot) of entry `key` of a tile from its lookup slot,
+// or -1 when the entry is skipped.
+__device__ inline int ws_sparse_row(const uint8_t* slot, int key, int sk, int num_pages) {
+  const int j = reinterpret_cast<const int32_t*>(slot)[key];
+  const int page = reinterpret_cast<const int32_t*>(slot + 256)[key];
+  return j >= 0 && j < sk && page >= 0 && page < num_pages ? page * kKeys + (j & (kKeys - 1)) : -1;
+}
+
+// The sparse tile's copies of slice e (as ws_issue_nope_slice: lane l moves
+// position l % 4 of key 16 i + l / 4) and of rope rows 8e..8e+7 (as
+// ws_issue_rope), each lane from its entry's cache row, or zeros: always
+// 4 + (rope ? 1 : 0) copy instructions on all lanes.
+template <int ROPE>
+__device__ __attribute__((always_inline)) inline void ws_issue_sparse_nope(uint8_t* lds, int bufi, const uint8_t* kv,
+                                                                           const uint8_t* slot, int sk, int num_pages,
+                                                                           int e) {
+  constexpr long RB = kNope + 2 * ROPE;
+  const int lane = fresh_lane();
+  uint8_t* dst = lds + bufi * kNopeRegion + e * 4096;
+  const unsigned chunk16 = 16u * (unsigned)((lane & 3) ^ (lane >> 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cr = ws_sparse_row(slot, 16 * i + (lane >> 2), sk, num_pages);
+    const uint8_t* src = cr >= 0 ? kv + (long)cr * RB + 64 * e + chunk16 : kWsZeros + 16 * lane;
+    load_lds16(src, dst + i * 1024);
+  }
+}
+template <int ROPE>
+__device__ __attribute__((always_inline)) inline void ws_issue_sparse_rope(uint8_t* lds, int bufi, const uint8_t* kv,
+                                                                           const uint8_t* slot, int sk, int num_pages,
+                                                                           int e) {
+  constexpr long RB = kNope + 2 * ROPE;
+  const int lane = fresh_lane();
+  const int row = 8 * e + (lane >> 3);
+  const int cr = ws_sparse_row(slot, row, sk, num_pages);
+  const unsigned c16 = 16u * (unsigned)((lane & 7) ^ ((row >> 1) & 7));
+  const uint8_t* src = cr >= 0 ? kv + (long)cr * RB + kNope + c16 : kWsZeros + 16 * lane;
+  load_lds16(src, lds + kRopeBase + bufi * kRopeRegion + e * 1024);
+}
+
 // gfx942's e4m3fnuz codes turned into OCP e4m3fn codes (fnuz4_to_ocp4), in
 // place in this wave's 4 KiB slice of a landed tile: the fp8 matrix cores read
 // OCP codes only.
@@ -170,12 +228,14 @@ __device__ inline void ws_fnuz_to_ocp_slice(uint8_t* lds, int bufi, int e) {
   }
 }
 
-template <int ROPE, bool FNUZ>
+template <int ROPE, bool FNUZ, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(3, 3)))
 void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   constexpr int D = kNope + ROPE;   // q row length
   constexpr long RB = kNope + 2 * ROPE;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes];
+  constexpr int kSpBytes = SPARSE ? kSpSlots * kSpSlotBytes : 0;
+  static_assert(WsQ<ROPE>::lds_bytes + kSpBytes <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes + kSpBytes];
   uint8_t* const lds = lds_;
   uint8_t* const xp = lds + Tile<ROPE>::lds_bytes;
   float* const xalpha = reinterpret_cast<float*>(xp + 2 * WsX::p_bytes);
@@ -195,16 +255,35 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   const int s = bid % a.splits;
   const int g = bid / a.splits;
 
-  int sk = seq_lens[g];
+  // dense: g is a sequence, its key stream the sequence's pages; sparse: g
+  // is a query token (sequence g / s_q), its key stream the token's index
+  // list in 64-entry units
+  const int b = SPARSE ? g / a.s_q : g;
+  int sk = seq_lens[b];
   sk = max(0, min(sk, a.max_pages * kKeys));
-  const int units = (sk + kKeys - 1) / kKeys;
+  const int units = SPARSE ? (a.topk + kKeys - 1) / kKeys : (sk + kKeys - 1) / kKeys;
   const int u0 = (int)((long)s * units / a.splits);
   const int u1 = (int)((long)(s + 1) * units / a.splits);
   const int ntiles = u1 - u0;
-  const int32_t* bt_row = block_table + (long)g * a.max_pages;
+  const int32_t* bt_row = block_table + (long)b * a.max_pages;
   // page id of unit u0 + t (uniform: a scalar load)
   auto page_at = [&](int t) -> int { return u0 + t < u1 ? bt_row[u0 + t] : -1; };
   auto page_valid = [&](int page) -> bool { return page >= 0 && page < a.num_pages; };
+  // sparse: the lookup slot of tile t, and the two DMA steps that fill it
+  // (the caller's wave issues them; see kSpSlots)
+  uint8_t* const sp_base = lds + WsQ<ROPE>::lds_bytes;
+  auto sp_slot = [&](int t) -> uint8_t* { return sp_base + (t % kSpSlots) * kSpSlotBytes; };
+  auto sp_dma_index = [&](int t) {
+    const int32_t* idx_row = indices + (long)g * a.topk;
+    const int e = (u0 + t) * kKeys + fresh_lane();
+    const int32_t* src = e < a.topk ? idx_row + e : kWsMinusOne;
+    load_lds4_gather(reinterpret_cast<const float*>(src), sp_slot(t));
+  };
+  auto sp_dma_page = [&](int t) {   // the index of tile t has landed
+    const int j = reinterpret_cast<const int32_t*>(sp_slot(t))[fresh_lane()];
+    const int32_t* src = j >= 0 && j < sk ? bt_row + (j >> 6) : kWsMinusOne;
+    load_lds4_gather(reinterpret_cast<const float*>(src), sp_slot(t) + 256);
+  };
 
   if (wave < kSWaves) {
     // ======================= S-wave: S^T, softmax, P^T ========================
@@ -268,7 +347,13 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       __syncthreads();   // tile k landed; P^T of tile k-2's parity is free again
       if (k == ntiles) break;
       const int par = k & 1;
-      const int page_cur = page_at(k);   // needed after the products
+      if (!wave_active) {   // a row block past the problem: the barriers only
+        if (fresh_lane() == 0) xflag[4 * par + wave] = 0;
+        continue;
+      }
+      const int page_cur = SPARSE ? 0 : page_at(k);   // needed after the products
+      // sparse: whether entry `lane` of tile k names a cache row
+      const bool sp_ok = SPARSE ? ws_sparse_row(sp_slot(k), fresh_lane(), sk, a.num_pages) >= 0 : false;
       const uint8_t* nope = lds + buf * kNopeRegion;
       const uint8_t* rope = lds + kRopeBase + buf * kRopeRegion;
       const int unit = u0 + k;
@@ -335,9 +420,25 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
 
       // ---- mask + online softmax (log2 domain), P^T to LDS ----------------------
       const bool page_ok = page_valid(page_cur);
-      const bool full = page_ok && (unit + 1) * kKeys <= sk - (a.causal ? a.s_q - 1 : 0);
+      const unsigned long long smask = SPARSE ? __ballot(sp_ok) : 0ull;
+      const bool full = SPARSE ? smask == ~0ull : page_ok && (unit + 1) * kKeys <= sk - (a.causal ? a.s_q - 1 : 0);
       const int limit = page_ok ? row_len - unit * kKeys : 0;
-      if (!full) {
+      if (SPARSE && !full) {
+        // register r of key block kb is key 32 kb + 8 j + 4 ((j + h) & 1) + r % 4:
+        // the upper lane half takes the mask with the two 4-key halves of every
+        // 8-key group swapped, so that every bit position is a compile-time offset
+        const bool hl = (fresh_lane() >> 5) != 0;
+        const unsigned long long sw = ((smask & 0x0F0F0F0F0F0F0F0Full) << 4) | ((smask >> 4) & 0x0F0F0F0F0F0F0F0Full);
+        const unsigned long long m = hl ? sw : smask;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = r >> 2;
+            const int kc = 32 * kb + 8 * j + 4 * (j & 1) + (r & 3);
+            acc[kb][r] = ((m >> kc) & 1ull) ? acc[kb][r] : -INFINITY;
+          }
+      } else if (!full) {
         // register r of key block kb is key 32 kb + 8 j + 4 ((j + h) & 1) + r % 4
         // (j = r / 4): compile-time offsets against two per-lane limits, so
         // that no per-lane key index is kept across the tile loop
@@ -436,8 +537,17 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     };
     // tile 0 before the loop, tile 1 once tile 0 has landed (which keeps the
     // prologue's burst of query and tile loads small); then tile k+2 during
-    // iteration k
-    if (ntiles > 0) {
+    // iteration k. Sparse: the first wave fills the lookup slots of tiles
+    // 0..3 (indices) and 0..2 (pages) first, and tile 0 follows the barrier
+    // that publishes them.
+    if constexpr (SPARSE) {
+      if (e == 0) {
+        for (int t = 0; t < 4 && t < ntiles; ++t) sp_dma_index(t);
+        wait_vmcnt<0>();
+        for (int t = 0; t < 3 && t < ntiles; ++t) sp_dma_page(t);
+        wait_vmcnt<0>();
+      }
+    } else if (ntiles > 0) {
       int valid;
       const uint8_t* src = tile_src(0, page_at(0), valid);
       if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 0, src, valid, e);
@@ -454,15 +564,26 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       if (qq == 0) qexp[qrl] = q_ok ? qe : 0;
     }
     __syncthreads();   // the quantized query rows are staged
+    if constexpr (SPARSE) {
+      if (ntiles > 0) {
+        if constexpr (ROPE > 0) ws_issue_sparse_rope<ROPE>(lds, 0, kv, sp_slot(0), sk, a.num_pages, e);
+        ws_issue_sparse_nope<ROPE>(lds, 0, kv, sp_slot(0), sk, a.num_pages, e);
+      }
+    }
     wait_vmcnt<0>();   // tile 0 has landed
     if constexpr (FNUZ) {
       if (ntiles > 0) ws_fnuz_to_ocp_slice(lds, 0, e);
     }
     if (ntiles > 1) {   // tile 1 must land by the end of iteration 0
-      int valid1;
-      const uint8_t* src1 = tile_src(1, page_at(1), valid1);
-      if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 1, src1, valid1, e);
-      ws_issue_nope_slice<ROPE>(lds, 1, src1, valid1, e);
+      if constexpr (SPARSE) {
+        if constexpr (ROPE > 0) ws_issue_sparse_rope<ROPE>(lds, 1, kv, sp_slot(1), sk, a.num_pages, e);
+        ws_issue_sparse_nope<ROPE>(lds, 1, kv, sp_slot(1), sk, a.num_pages, e);
+      } else {
+        int valid1;
+        const uint8_t* src1 = tile_src(1, page_at(1), valid1);
+        if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 1, src1, valid1, e);
+        ws_issue_nope_slice<ROPE>(lds, 1, src1, valid1, e);
+      }
     }
 
     // V^T lane base (slice layout): lane group g = lane / 16 reads chunk
@@ -483,13 +604,23 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       for (int r = 0; r < kSWaves; ++r) O[j][r] = f32x16{};
 
     int bufp = 2;   // ring slot of tile k-1 (= slot of tile k+2)
-    int page2 = page_at(2);   // page id of tile k+2, loaded one iteration ahead
+    int page2 = SPARSE ? -1 : page_at(2);   // page id of tile k+2, loaded one iteration ahead
     for (int k = 0; k <= ntiles; ++k) {
       __syncthreads();   // tile k has landed in every wave's share
       const bool next2 = k + 2 < ntiles;
       int valid2 = 0;
       const uint8_t* src2 = nullptr;
-      if (next2) {
+      if constexpr (SPARSE) {
+        // lookups one iteration ahead of their use, issued before this
+        // iteration's copies so that the wait below covers them
+        if (e == 0) {
+          if (k + 3 < ntiles) sp_dma_page(k + 3);
+          if (k + 4 < ntiles) sp_dma_index(k + 4);
+        }
+        if constexpr (ROPE > 0) {
+          if (next2) ws_issue_sparse_rope<ROPE>(lds, bufp, kv, sp_slot(k + 2), sk, a.num_pages, e);
+        }
+      } else if (next2) {
         src2 = tile_src(k + 2, page2, valid2);
         page2 = page_at(k + 3);
         if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, bufp, src2, valid2, e);   // S^T(k-1) released it
@@ -510,7 +641,8 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       if (next2) {
         // this wave's slice of tile k-1 has been read: refill it with tile k+2
         if (k > 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(vr[0]), "+v"(vr[1]) :: "memory");
-        ws_issue_nope_slice<ROPE>(lds, bufp, src2, valid2, e);
+        if constexpr (SPARSE) ws_issue_sparse_nope<ROPE>(lds, bufp, kv, sp_slot(k + 2), sk, a.num_pages, e);
+        else ws_issue_nope_slice<ROPE>(lds, bufp, src2, valid2, e);
       }
       if (k > 0) {
         const int pp = (k - 1) & 1;
@@ -536,6 +668,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         const int lo16 = fresh_lane() * 16;
 #pragma unroll
         for (int r = 0; r < kSWaves; ++r) {
+          if (rg * kSWaves + r >= a.row_blocks) break;   // row blocks past the problem: nothing to add
           const i32x4 lo = lds_ld16(pprev, r * 2048 + lo16);
           const i32x4 hi = lds_ld16(pprev, r * 2048 + 1024 + lo16);
           const i32x8 pt = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -544,8 +677,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // tile k+1 must have landed before the next barrier; tile k+2 may stay in flight
-      if (next2 && valid2 == kKeys) wait_vmcnt<kCopies>();
+      // tile k+1 must have landed before the next barrier; tile k+2 may stay in
+      // flight (sparse tiles always take kCopies instructions)
+      if (next2 && (SPARSE || valid2 == kKeys)) wait_vmcnt<kCopies>();
       else wait_vmcnt<0>();
       if constexpr (FNUZ) {
         if (k + 1 < ntiles) ws_fnuz_to_ocp_slice(lds, (k + 1) % kBufs, e);
@@ -642,20 +776,26 @@ hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table,
 }
 
 bool decode_ws_eligible(const DecodeLaunch& d) {
-  if (d.dot != DOT_FP8 || d.per_token || d.topk != 0 || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
-  // an fnuz cache with fp8 dots runs here at any row count (the only kernel that reads it with fp8 dots)
+  if (d.dot != DOT_FP8 || d.per_token || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
+  // sparse: at any row count (a one-wave workgroup per 16-head token is the
+  // alternative); an fnuz cache with fp8 dots runs here at any row count (the
+  // only kernel that reads it with fp8 dots; sparse fnuz is refused earlier)
+  if (d.topk != 0) return !d.fnuz;
   return d.fnuz || d.row_blocks >= 3;
 }
 
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
 #define MLA_WS_ARGS d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
-  if (d.d_rope == 64) {
-    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<64, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-    else hipLaunchKernelGGL((mla_decode_ws_kernel<64, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+  if (d.topk != 0) {
+    if (d.d_rope == 64) hipLaunchKernelGGL((mla_decode_ws_kernel<64, false, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    else hipLaunchKernelGGL((mla_decode_ws_kernel<0, false, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+  } else if (d.d_rope == 64) {
+    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<64, true, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    else hipLaunchKernelGGL((mla_decode_ws_kernel<64, false, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
   } else {
-    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<0, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-    else hipLaunchKernelGGL((mla_decode_ws_kernel<0, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<0, true, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    else hipLaunchKernelGGL((mla_decode_ws_kernel<0, false, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
   }
 #undef MLA_WS_ARGS
   return hipGetLastError();
