@@ -197,7 +197,9 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
   wait_vmcnt<0>();
   asm volatile("" : "+v"(pages_v));   // loaded before the loop, not inside it
 
-  const LdsBases lb(lane);
+  // sparse: the fragment bases are recomputed every tile from a fresh lane id
+  // (kept across the loop next to the sparse variant's state they spill)
+  LdsBases lb(lane);
 
   f32x16 O[16];
 #pragma unroll
@@ -219,6 +221,7 @@ void mla_decode_rows_kernel(MLA_KERNEL_PTRS, KDims a) {
     const int buf_next = buf == kBufs - 1 ? 0 : buf + 1;
     const int buf_next2 = buf_next == kBufs - 1 ? 0 : buf_next + 1;
     if constexpr (SPARSE) {
+      lb = LdsBases(lane_id_fresh());
       if (k + 1 < ntiles) {
         row_next = sparse_cache_row(j_b, pg_b);   // both landed by the wait above
         issue_sparse_scales(row_next, buf_next);

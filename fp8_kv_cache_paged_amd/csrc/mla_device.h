@@ -316,9 +316,14 @@ __device__ __attribute__((always_inline)) inline void issue_dense_tile(uint8_t* 
 // skipped entry (zero-filled).
 template <int ROPE, int NW>
 __device__ __attribute__((always_inline)) inline void issue_sparse_tile(uint8_t* lds, int bufi, const uint8_t* kv, int mine,
-                                         int lane, int wave) {
+                                         int, int wave) {
   constexpr int RB = kNope + 2 * ROPE;
-  const LoadOffsets<ROPE> lo = fresh_offsets<ROPE>(lane);
+  // a lane id the compiler cannot hoist out of the tile loop: the 32 lane
+  // exchange addresses derived from a kept one were spilled, and each reload
+  // waited for every copy in flight
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const LoadOffsets<ROPE> lo(lane);
   constexpr int NJ = 32 / NW, RJ = 8 / NW;
   uint8_t* nope = lds + bufi * kNopeRegion + wave * NJ * 1024;
   uint8_t* rope = lds + kRopeBase + bufi * kRopeRegion + wave * RJ * 1024;
@@ -330,6 +335,9 @@ __device__ __attribute__((always_inline)) inline void issue_sparse_tile(uint8_t*
       load_lds16(kv + (long)cr * RB + (lo.nope_lane(jj & 7) - (lane >> 5) * RB), nope + jj * 1024);
     else
       lds_zero16(nope + jj * 1024 + lane * 16);
+    // one copy's address at a time (with all of a one-wave tile's copies
+    // computed up front the row-block kernel spills)
+    __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (ROPE > 0) {
 #pragma unroll
@@ -489,6 +497,16 @@ __device__ inline int vt_lane_base(int lane, int b8) {
   const int tk = tr_key(sup >> 1, h);
   return tk * kNope + (((2 * b8 + (g & 1)) ^ (tk & 15)) << 4) + 8 * (sup & 1);
 }
+// The lane id from the exec-mask bit count, as volatile asm: a value the
+// compiler recomputes where it is used instead of keeping it (and what is
+// derived from it) across a tile loop, where register pressure would spill it
+// and each reload would wait for every tile copy in flight.
+__device__ inline int lane_id_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 struct LdsBases {
   int k8[4][2], k16[8], rp[4], vt[8];
   __device__ LdsBases(int lane) {
