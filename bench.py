@@ -359,9 +359,8 @@ def main():
     gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     mfma_peak = FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS
     if args.dot == "fp8":
-        # the role-split kernel: per-tensor scales, dense with >= 3 row blocks, any sparse shape, any fnuz
-        ws_path = not per_token and (idx is not None or (w.s_q * w.h_q + 31) // 32 >= 3
-                                     or args.kv_encoding == "e4m3fnuz")
+        # the role-split kernel: dense with >= 3 row blocks, any sparse shape, any fnuz cache
+        ws_path = idx is not None or (w.s_q * w.h_q + 31) // 32 >= 3 or args.kv_encoding == "e4m3fnuz"
         kernel_name = "mla_decode_ws_kernel" if ws_path else "mla_decode_kernel"
     else:
         kernel_name = "mla_decode_kernel or mla_decode_rows_kernel"

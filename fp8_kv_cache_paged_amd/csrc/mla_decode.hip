@@ -1468,6 +1468,7 @@ static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t s
 template <int DOT, int ROPE, bool SPARSE>
 static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   if constexpr (DOT == DOT_FP8) {
+    if (decode_ws_eligible(d)) return launch_decode_ws(d, a, st);
     if (d.per_token) {
       const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
       switch (waves_per_group(d.row_blocks)) {
@@ -1482,7 +1483,6 @@ static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t s
     }
   }
   if constexpr (DOT == DOT_FP8) {
-    if (decode_ws_eligible(d)) return launch_decode_ws(d, a, st);
     if (d.rows_kernel) return launch_nw<DOT, ROPE, SPARSE, false, false>(d, a, st);
     return d.gather_v ? launch_nw<DOT, ROPE, SPARSE, true, true>(d, a, st)
                       : launch_nw<DOT, ROPE, SPARSE, false, true>(d, a, st);

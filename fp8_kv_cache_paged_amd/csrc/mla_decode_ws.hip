@@ -228,14 +228,15 @@ __device__ inline void ws_fnuz_to_ocp_slice(uint8_t* lds, int bufi, int e) {
   }
 }
 
-template <int ROPE, bool FNUZ, bool SPARSE>
+template <int ROPE, bool FNUZ, bool SPARSE, bool PT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(3, 3)))
 void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   constexpr int D = kNope + ROPE;   // q row length
   constexpr long RB = kNope + 2 * ROPE;
   constexpr int kSpBytes = SPARSE ? kSpSlots * kSpSlotBytes : 0;
-  static_assert(WsQ<ROPE>::lds_bytes + kSpBytes <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes + kSpBytes];
+  constexpr int kPtBytes = PT ? kBufs * 512 : 0;   // per ring slot: 64 k-scales, 64 v-scales
+  static_assert(WsQ<ROPE>::lds_bytes + kSpBytes + kPtBytes <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes + kSpBytes + kPtBytes];
   uint8_t* const lds = lds_;
   uint8_t* const xp = lds + Tile<ROPE>::lds_bytes;
   float* const xalpha = reinterpret_cast<float*>(xp + 2 * WsX::p_bytes);
@@ -272,6 +273,8 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   // sparse: the lookup slot of tile t, and the two DMA steps that fill it
   // (the caller's wave issues them; see kSpSlots)
   uint8_t* const sp_base = lds + WsQ<ROPE>::lds_bytes;
+  // per-token scales: the 64 k-scales and 64 v-scales of the tile in ring slot b
+  float* const pt_base = reinterpret_cast<float*>(lds + WsQ<ROPE>::lds_bytes + kSpBytes);
   auto sp_slot = [&](int t) -> uint8_t* { return sp_base + (t % kSpSlots) * kSpSlotBytes; };
   auto sp_dma_index = [&](int t) {
     const int32_t* idx_row = indices + (long)g * a.topk;
@@ -302,7 +305,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) qr_raw[t] = *reinterpret_cast<const i32x4*>(qsrc + kNope + 16 * t + 8 * h);
     }
-    const float k_scale_v = *k_scale;
+    const float k_scale_v = PT ? 1.f : *k_scale;   // per token: the k-scales apply per key
     const int i_tok = row / a.h_q;
     const int row_len = row_ok ? (a.causal ? sk - (a.s_q - 1 - i_tok) : sk) : 0;   // keys this row may see
     wait_vmcnt<0>();
@@ -341,6 +344,24 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     const float zscale = ROPE > 0 ? a.sm_log2 : fmaxf(qk_scale * a.sm_log2, 1e-37f);
     float m_run = -INFINITY;   // max used for the exponentials (log2 domain)
     float l_run = 0.f;         // this lane's share of the running sum
+    // Per-token scales: P is packed as p * v_j / v_run, v_run a reference
+    // v-scale raised lazily (to the tile's largest when a key's v-scale
+    // exceeds 1.5 v_run, so that P stays <= 1.5 * 2^8 = 384 < 448); O carries
+    // v_run and is rescaled by v_old / v_new when it rises.
+    float v_run = 0.f, inv_vrun = 0.f;
+    // k-scales of the lane's keys of key block kb (register r: key 32 kb + 8 j
+    // + 4 ((j + h) & 1) + r % 4, j = r / 4), four per read
+    // (one read in flight at a time: the S-wave's registers are full here)
+    auto scale_by_k = [&](f32x16& acc_kb, int kb, const float* ks, float f) {
+      const int hh = fresh_lane() >> 5;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(ks + 32 * kb + 8 * j + 4 * ((j + hh) & 1));
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc_kb[4 * j + rr] *= k4[rr] * f;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 
     int buf = 0;
     for (int k = 0; k <= ntiles; ++k) {
@@ -400,10 +421,15 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
               if (f == NN - 1) {
                 // nope sums complete: scale them, then add the rope products
                 s_nop_result2(acc[0], acc[1]);
+                if constexpr (PT) {
+                  scale_by_k(acc[0], 0, pt_base + buf * 128, qk_scale);
+                  scale_by_k(acc[1], 1, pt_base + buf * 128, qk_scale);
+                } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  acc[0][r] *= qk_scale;
-                  acc[1][r] *= qk_scale;
+                  for (int r = 0; r < 16; ++r) {
+                    acc[0][r] *= qk_scale;
+                    acc[1][r] *= qk_scale;
+                  }
                 }
               }
             }
@@ -417,6 +443,10 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       }
       s_nop_result2(acc[0], acc[1]);
       __builtin_amdgcn_s_setprio(0);
+      if constexpr (PT && ROPE == 0) {   // rope-free: q_scale rides on zscale
+        scale_by_k(acc[0], 0, pt_base + buf * 128, 1.f);
+        scale_by_k(acc[1], 1, pt_base + buf * 128, 1.f);
+      }
 
       // ---- mask + online softmax (log2 domain), P^T to LDS ----------------------
       const bool page_ok = page_valid(page_cur);
@@ -460,23 +490,46 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
       mx = pair_max_swap(mx) * zscale;
 
+      // per-token scales: raise v_run when a key of this tile (key = lane)
+      // exceeds 1.5 v_run (always at the first tile with a key)
+      float vfac = 1.f;   // v_old / v_new for O, 1 when v_run stays or was 0
+      bool vraise = false;
+      if constexpr (PT) {
+        const int lk = fresh_lane();
+        const bool exists = SPARSE ? sp_ok : page_ok && lk < min(kKeys, sk - unit * kKeys);
+        const float vmine = exists ? pt_base[buf * 128 + 64 + lk] : 0.f;
+        if (__ballot(vmine > 1.5f * v_run)) {
+          float vm = vmine;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) vm = fmaxf(vm, __shfl_xor(vm, o));
+          vm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, vm)));
+          vraise = v_run > 0.f;
+          vfac = vraise ? v_run / vm : 1.f;
+          v_run = vm;
+          inv_vrun = 1.f / vm;
+        }
+      }
       const bool raise = mx > m_run + Soft<DOT_FP8>::tau;
       bool flagged = false;
-      if (__ballot(raise)) {
+      if (__ballot(raise) || vraise) {
         const float m_new = raise ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+        // 0 for a row that has seen no key (its O and l are 0; the difference
+        // of two infinities would give NaN)
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
-        // O needs rescaling only where a finite max was raised
-        flagged = __ballot(raise && m_run != -INFINITY) != 0ull;
+        // O needs rescaling only where a finite max was raised, or (all rows)
+        // where v_run rose
+        flagged = vraise || __ballot(raise && m_run != -INFINITY) != 0ull;
         if (flagged) {
           const int ln = fresh_lane();
-          if (ln < 32) xalpha[par * (kSWaves * 32) + wave * 32 + ln] = alpha;
+          if (ln < 32) xalpha[par * (kSWaves * 32) + wave * 32 + ln] = alpha * vfac;
         }
         m_run = m_new;
       }
       const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT_FP8>::ps_log2;
       float psum = 0.f;
       i32x8 pb;
+      const int hv = fresh_lane() >> 5;
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const int kb = q4 >> 2, r0 = 4 * (q4 & 3);
@@ -485,6 +538,14 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         for (int r = 0; r < 4; ++r) {
           pe[r] = __builtin_amdgcn_exp2f(fmaf(acc[kb][r0 + r], zscale, -m_exp));
           psum += pe[r];
+        }
+        if constexpr (PT) {
+          // p times its key's v-scale / v_run; masked keys (p = 0) skip the
+          // scale, which may be stale
+          const int j = q4 & 3;
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(pt_base + buf * 128 + 64 + 32 * kb + 8 * j + 4 * ((j + hv) & 1));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pe[r] = pe[r] > 0.f ? pe[r] * (v4[r] * inv_vrun) : 0.f;
         }
         pb[q4] = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
       }
@@ -500,15 +561,18 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // ---- epilogue: per-row output scale for the PV-waves; lse ---------------------
     const float l_tot = pair_sum_swap(l_run);
     const bool nonempty = l_tot > 0.f;
-    // splits == 1: v_scale / l; else the partials' 1 / l (fp16 partials,
-    // |value| <= 448; the combine applies v_scale)
-    if (h == 0) xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? *v_scale : 1.f) / l_tot : 0.f;
+    // splits == 1: (v_scale, or per token v_run) / l; else the partials' 1 / l
+    // (fp16 partials in code units, |value| <= 448; the combine applies
+    // v_scale, or the per-row v_run stored beside the lse)
+    if (h == 0) xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? (PT ? v_run : *v_scale) : 1.f) / l_tot : 0.f;
     if (wave_active && h == 0) {
       const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT_FP8>::ps_log2 : -INFINITY;
       if (a.splits == 1) {
         if (row_ok) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
       } else {
-        part_lse[(((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n] = lse2;
+        const long prow = (((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n;
+        part_lse[prow] = lse2;
+        if constexpr (PT) part_row_scale(part_lse, a)[prow] = v_run;
       }
     }
     __syncthreads();
@@ -535,6 +599,25 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       valid = ok ? min(kKeys, sk - (u0 + t) * kKeys) : 0;
       return kv + (long)(ok ? page : 0) * kKeys * RB;
     };
+    // per-token scales of tile t (dense: its page id) into ring slot bufi:
+    // the k-scales by wave 1, the v-scales by wave 2, one 4-byte-per-lane copy
+    // each (a missing page's keys are masked and its scales never read)
+    constexpr bool kPtWave = PT;
+    const bool pt_wave = kPtWave && (e == 1 || e == 2);
+    auto issue_pt = [&](int t, int bufi, int page) {
+      if constexpr (PT) {
+        if (pt_wave) {
+          const float* sc = e == 1 ? k_scale : v_scale;
+          uint8_t* dst = reinterpret_cast<uint8_t*>(pt_base + bufi * 128 + (e == 2 ? 64 : 0));
+          if constexpr (SPARSE) {
+            const int cr = ws_sparse_row(sp_slot(t), fresh_lane(), sk, a.num_pages);
+            load_lds4_gather(cr >= 0 ? sc + cr : reinterpret_cast<const float*>(kWsMinusOne), dst);
+          } else if (page_valid(page)) {
+            load_lds4_row(sc + (long)page * kKeys, dst);
+          }
+        }
+      }
+    };
     // tile 0 before the loop, tile 1 once tile 0 has landed (which keeps the
     // prologue's burst of query and tile loads small); then tile k+2 during
     // iteration k. Sparse: the first wave fills the lookup slots of tiles
@@ -549,7 +632,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       }
     } else if (ntiles > 0) {
       int valid;
-      const uint8_t* src = tile_src(0, page_at(0), valid);
+      const int page0 = page_at(0);
+      const uint8_t* src = tile_src(0, page0, valid);
+      issue_pt(0, 0, page0);
       if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 0, src, valid, e);
       ws_issue_nope_slice<ROPE>(lds, 0, src, valid, e);
     }
@@ -566,6 +651,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     __syncthreads();   // the quantized query rows are staged
     if constexpr (SPARSE) {
       if (ntiles > 0) {
+        issue_pt(0, 0, 0);
         if constexpr (ROPE > 0) ws_issue_sparse_rope<ROPE>(lds, 0, kv, sp_slot(0), sk, a.num_pages, e);
         ws_issue_sparse_nope<ROPE>(lds, 0, kv, sp_slot(0), sk, a.num_pages, e);
       }
@@ -576,11 +662,14 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     if (ntiles > 1) {   // tile 1 must land by the end of iteration 0
       if constexpr (SPARSE) {
+        issue_pt(1, 1, 0);
         if constexpr (ROPE > 0) ws_issue_sparse_rope<ROPE>(lds, 1, kv, sp_slot(1), sk, a.num_pages, e);
         ws_issue_sparse_nope<ROPE>(lds, 1, kv, sp_slot(1), sk, a.num_pages, e);
       } else {
         int valid1;
-        const uint8_t* src1 = tile_src(1, page_at(1), valid1);
+        const int page1 = page_at(1);
+        const uint8_t* src1 = tile_src(1, page1, valid1);
+        issue_pt(1, 1, page1);
         if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, 1, src1, valid1, e);
         ws_issue_nope_slice<ROPE>(lds, 1, src1, valid1, e);
       }
@@ -617,11 +706,13 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           if (k + 3 < ntiles) sp_dma_page(k + 3);
           if (k + 4 < ntiles) sp_dma_index(k + 4);
         }
+        if (next2) issue_pt(k + 2, bufp, 0);
         if constexpr (ROPE > 0) {
           if (next2) ws_issue_sparse_rope<ROPE>(lds, bufp, kv, sp_slot(k + 2), sk, a.num_pages, e);
         }
       } else if (next2) {
         src2 = tile_src(k + 2, page2, valid2);
+        issue_pt(k + 2, bufp, page2);   // S^T(k-1) read the slot's scales before the barrier
         page2 = page_at(k + 3);
         if constexpr (ROPE > 0) ws_issue_rope<ROPE>(lds, bufp, src2, valid2, e);   // S^T(k-1) released it
       }
@@ -678,9 +769,14 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         }
       }
       // tile k+1 must have landed before the next barrier; tile k+2 may stay in
-      // flight (sparse tiles always take kCopies instructions)
-      if (next2 && (SPARSE || valid2 == kKeys)) wait_vmcnt<kCopies>();
-      else wait_vmcnt<0>();
+      // flight (sparse tiles always take kCopies instructions, plus the
+      // per-token scale copy of waves 1 and 2)
+      if (next2 && (SPARSE || valid2 == kKeys)) {
+        if (pt_wave) wait_vmcnt<kCopies + 1>();
+        else wait_vmcnt<kCopies>();
+      } else {
+        wait_vmcnt<0>();
+      }
       if constexpr (FNUZ) {
         if (k + 1 < ntiles) ws_fnuz_to_ocp_slice(lds, (k + 1) % kBufs, e);
       }
@@ -776,10 +872,11 @@ hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table,
 }
 
 bool decode_ws_eligible(const DecodeLaunch& d) {
-  if (d.dot != DOT_FP8 || d.per_token || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
+  if (d.dot != DOT_FP8 || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
   // sparse: at any row count (a one-wave workgroup per 16-head token is the
   // alternative); an fnuz cache with fp8 dots runs here at any row count (the
-  // only kernel that reads it with fp8 dots; sparse fnuz is refused earlier)
+  // only kernel that reads it with fp8 dots; sparse or per-token fnuz is
+  // refused earlier); dense otherwise from three row blocks up
   if (d.topk != 0) return !d.fnuz;
   return d.fnuz || d.row_blocks >= 3;
 }
@@ -787,16 +884,23 @@ bool decode_ws_eligible(const DecodeLaunch& d) {
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
 #define MLA_WS_ARGS d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
+#define MLA_WS_LAUNCH(R, F, S, P) \
+  hipLaunchKernelGGL((mla_decode_ws_kernel<R, F, S, P>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a)
+  const bool r64 = d.d_rope == 64;
   if (d.topk != 0) {
-    if (d.d_rope == 64) hipLaunchKernelGGL((mla_decode_ws_kernel<64, false, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-    else hipLaunchKernelGGL((mla_decode_ws_kernel<0, false, true>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-  } else if (d.d_rope == 64) {
-    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<64, true, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-    else hipLaunchKernelGGL((mla_decode_ws_kernel<64, false, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    if (d.per_token) {
+      if (r64) MLA_WS_LAUNCH(64, false, true, true); else MLA_WS_LAUNCH(0, false, true, true);
+    } else {
+      if (r64) MLA_WS_LAUNCH(64, false, true, false); else MLA_WS_LAUNCH(0, false, true, false);
+    }
+  } else if (d.per_token) {
+    if (r64) MLA_WS_LAUNCH(64, false, false, true); else MLA_WS_LAUNCH(0, false, false, true);
+  } else if (d.fnuz) {
+    if (r64) MLA_WS_LAUNCH(64, true, false, false); else MLA_WS_LAUNCH(0, true, false, false);
   } else {
-    if (d.fnuz) hipLaunchKernelGGL((mla_decode_ws_kernel<0, true, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
-    else hipLaunchKernelGGL((mla_decode_ws_kernel<0, false, false>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a);
+    if (r64) MLA_WS_LAUNCH(64, false, false, false); else MLA_WS_LAUNCH(0, false, false, false);
   }
+#undef MLA_WS_LAUNCH
 #undef MLA_WS_ARGS
   return hipGetLastError();
 }
