@@ -41,10 +41,8 @@ int32_t validate(const mla_params* p) {
       break;
     case MLA_KV_FP8_E4M3FNUZ:
       // per-tensor scales; bf16 dots decode the codes in registers, fp8 dots
-      // (dense only) transcode each landed tile to the e4m3fn codes of the
-      // same values
+      // transcode each landed tile to the e4m3fn codes of the same values
       if (p->kv_scale_per_token != 0) return MLA_ERR_UNSUPPORTED;
-      if (p->dot == MLA_DOT_FP8 && p->topk > 0) return MLA_ERR_UNSUPPORTED;
       break;
     case MLA_KV_FP8_E5M2:
     case MLA_KV_INT8:

@@ -875,9 +875,9 @@ bool decode_ws_eligible(const DecodeLaunch& d) {
   if (d.dot != DOT_FP8 || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
   // sparse: at any row count (a one-wave workgroup per 16-head token is the
   // alternative); an fnuz cache with fp8 dots runs here at any row count (the
-  // only kernel that reads it with fp8 dots; sparse or per-token fnuz is
-  // refused earlier); dense otherwise from three row blocks up
-  if (d.topk != 0) return !d.fnuz;
+  // only kernel that reads it with fp8 dots; per-token fnuz is refused
+  // earlier); dense otherwise from three row blocks up
+  if (d.topk != 0) return true;
   return d.fnuz || d.row_blocks >= 3;
 }
 
@@ -890,6 +890,8 @@ hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t s
   if (d.topk != 0) {
     if (d.per_token) {
       if (r64) MLA_WS_LAUNCH(64, false, true, true); else MLA_WS_LAUNCH(0, false, true, true);
+    } else if (d.fnuz) {
+      if (r64) MLA_WS_LAUNCH(64, true, true, false); else MLA_WS_LAUNCH(0, true, true, false);
     } else {
       if (r64) MLA_WS_LAUNCH(64, false, true, false); else MLA_WS_LAUNCH(0, false, true, false);
     }

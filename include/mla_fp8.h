@@ -87,7 +87,7 @@ extern "C" {
  * by both dot modes. gfx942's e4m3fnuz (bias 8, largest magnitude 240, NaN
  * only at 0x80; ROCm/aiter PR #6199, Technical details) is read with
  * per-tensor scales only. MLA_DOT_BF16 decodes its codes exactly to bf16 in
- * registers. MLA_DOT_FP8 (dense only; sparse is MLA_ERR_UNSUPPORTED) turns
+ * registers. MLA_DOT_FP8 (dense and sparse) turns
  * each landed tile's codes into the e4m3fn codes of the same values for the
  * OCP fp8 matrix cores: exact for every magnitude from 2^-6 to 240 (in units
  * of the scale); the fnuz magnitudes below 2^-6 (steps of 2^-10) go to
@@ -97,7 +97,7 @@ extern "C" {
  * misread (ROCm/aiter PR #6199, the foreign-encoding refusal commit). */
 #define MLA_KV_FP8_E4M3FN 0
 #define MLA_KV_UINT8 1          /* raw bytes, taken to be e4m3fn */
-#define MLA_KV_FP8_E4M3FNUZ 2   /* per-tensor scales; fp8 dots dense only */
+#define MLA_KV_FP8_E4M3FNUZ 2   /* per-tensor scales */
 #define MLA_KV_FP8_E5M2 3       /* refused: MLA_ERR_UNSUPPORTED */
 #define MLA_KV_INT8 4           /* refused: MLA_ERR_UNSUPPORTED */
 #define MLA_KV_BF16 5           /* refused: MLA_ERR_UNSUPPORTED */

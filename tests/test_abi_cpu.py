@@ -53,7 +53,7 @@ def good(**kw):
     ({}, mla.MLA_OK),
     ({"kv_dtype": torch.float8_e4m3fn}, mla.MLA_OK),
     ({"kv_dtype": torch.float8_e4m3fnuz}, mla.MLA_OK),                         # fp8 dots (the default), dense
-    ({"kv_dtype": torch.float8_e4m3fnuz, "topk": 8, "d_rope": 0}, mla.MLA_ERR_UNSUPPORTED),   # fp8 dots, sparse
+    ({"kv_dtype": torch.float8_e4m3fnuz, "topk": 8, "d_rope": 0}, mla.MLA_OK),   # fp8 dots, sparse
     ({"kv_dtype": torch.float8_e4m3fnuz, "per_token_scales": True}, mla.MLA_ERR_UNSUPPORTED),
     ({"kv_dtype": torch.float8_e4m3fnuz, "dot": "bf16"}, mla.MLA_OK),           # decoded to bf16 in registers
     ({"kv_dtype": torch.float8_e4m3fnuz, "dot": "bf16", "per_token_scales": True}, mla.MLA_ERR_UNSUPPORTED),

@@ -7,12 +7,13 @@ the fnuz bit fields. Each workload's amax element carries the +-240 codes
 
 The bf16-dot path reads the cache exactly; every case checks that the kernel
 reads the +-240 codes as 240. 0x80, fnuz's NaN, reads as zero in both modes.
-The fp8-dot path (dense) turns each landed tile's codes into the e4m3fn codes
+The fp8-dot path turns each landed tile's codes into the e4m3fn codes
 of the same values (oracle.fp8.fnuz_as_e4m3fn, checked here bit for bit on
 all 256 codes): exact from 2^-6 of the scale up to 240, rounded to nearest
 even below. Its cases are held to the fp8 tolerances both against the oracle
 reading the fnuz cache exactly and against the oracle on the transcoded
-cache. Sparse fp8 dots refuse an fnuz cache (host check, no launch).
+cache, dense and sparse; per-token scales refuse an fnuz cache (host check,
+no launch).
 """
 
 import numpy as np
@@ -96,7 +97,7 @@ def test_fnuz_transcoding_is_bit_exact():
 
 
 @pytest.mark.parametrize("splits", [1, 3, 0])
-@pytest.mark.parametrize("idx", range(3))
+@pytest.mark.parametrize("idx", range(len(CASES)))
 def test_fnuz_parity_fp8_dots(idx, splits):
     name, kw = CASES[idx]
     w, oc, t = _case(name, **kw)
@@ -126,10 +127,18 @@ def test_fnuz_nan_code_reads_as_zero_fp8_dots():
     gu.compare(out, lse, *oc.exact, oc.qprime[1], "fp8", ref_out_rows=oc.qprime[0])
 
 
-def test_fnuz_cache_is_refused_with_sparse_fp8_dots():
-    name, kw = CASES[3]
+def test_fnuz_full_sparse_configuration_fp8_dots():
+    w, oc, t = _case("sparse")
+    res = gu.check(w, oc, "fp8", t=t)
+    print(f"fnuz sparse configuration fp8 dots: {res}")
+
+
+def test_fnuz_cache_is_refused_with_per_token_scales():
+    name, kw = CASES[0]
     w, oc, t = _case(name, **kw)
     assert t["kv"].dtype == torch.float8_e4m3fnuz
+    ks = torch.full((w.kv_cache.shape[0], 64), w.k_scale, dtype=torch.float32, device="cuda:0")
     with pytest.raises(mla.MlaError) as e:
-        gu.run(w, t, "fp8", num_splits=1)
+        mla.decode(t["q"], t["kv"], t["bt"], t["sl"], ks, ks.clone(), num_splits=1, dot="fp8", causal=w.causal,
+                   per_token_scales=True)
     assert e.value.status == mla.MLA_ERR_UNSUPPORTED
