@@ -80,8 +80,11 @@ int32_t resolve(const mla_params& p, int32_t num_splits, int32_t cu_count) {
     const long v = strtol(env, nullptr, 10);
     if (v > 0) return v > MLA_MAX_SPLITS ? MLA_MAX_SPLITS : (int32_t)v;
   }
-  // smallest s with groups * s >= CUs, capped at 16 and at the units per stream
-  const int32_t g = groups_of(p);
+  // smallest s with (workgroups per split) * s >= CUs, capped at 16 and at the
+  // units per stream; a split has one workgroup per key stream and group of
+  // four 32-row blocks (a prefill chunk's many rows already fill the chip)
+  const int32_t row_blocks = (rows_of(p) + 31) / 32;
+  const int32_t g = groups_of(p) * ((row_blocks + 3) / 4);
   int32_t s = cu_count > 0 ? (cu_count + g - 1) / g : 1;
   if (s > 16) s = 16;
   if (s > units) s = units;

@@ -145,9 +145,11 @@ MLA_API int32_t mla_fp8_validate(const mla_params* p);
  * workgroups, the split count comes from an automatic occupancy ("waves")
  * heuristic that leaves an already large grid unsplit, and an environment
  * variable overrides it. Here: num_splits > 0 is taken as given (capped at
- * MLA_MAX_SPLITS); 0 selects the smallest s with groups * s >= cu_count,
- * capped at 16 and at the number of 64-key units per sequence, where groups is
- * batch (dense) or batch * s_q (sparse). The environment variable
+ * MLA_MAX_SPLITS); 0 selects the smallest s with groups * row_groups * s >=
+ * cu_count, capped at 16 and at the number of 64-key units per sequence,
+ * where groups is batch (dense) or batch * s_q (sparse) and row_groups is
+ * ceil(rows / 128), rows = s_q * h_q (dense) or h_q (sparse): the workgroups
+ * one split launches. The environment variable
  * MLA_FP8_NUM_SPLITS, when set to a positive integer, replaces the automatic
  * choice. Returns a value >= 1, or a negative status on invalid *p. Host-only,
  * no HIP call. */

@@ -112,6 +112,16 @@ def test_auto_splits_sparse_counts_tokens_as_groups(L, monkeypatch):
     assert mla.resolve_splits(p, 0, 256) == 8          # 32 (sequence, token) streams
 
 
+def test_auto_splits_count_row_groups(L, monkeypatch):
+    # a prefill chunk: 2 sequences x 256 tokens x 16 heads = 32 groups of 128
+    # rows per sequence, so 64 workgroups per split and 4 splits fill 256 CUs
+    monkeypatch.delenv("MLA_FP8_NUM_SPLITS", raising=False)
+    p = good(batch=2, s_q=256, h_q=16, max_pages_per_seq=64)
+    assert mla.resolve_splits(p, 0, 256) == 4
+    q = good(batch=1, s_q=1024, h_q=64, max_pages_per_seq=64)   # 512 row groups: no split
+    assert mla.resolve_splits(q, 0, 256) == 1
+
+
 def test_explicit_and_env_splits(L, monkeypatch):
     p = good(max_pages_per_seq=200)
     assert mla.resolve_splits(p, 3, 256) == 3
