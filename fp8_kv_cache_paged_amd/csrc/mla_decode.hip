@@ -1221,10 +1221,14 @@ void mla_decode_kernel(MLA_KERNEL_PTRS, KDims a) {
 // values) issued together, and merged with a running max (every split
 // writes its partial, zeros when empty, so the loads need no guard).
 __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims a) {
-  const int gr = blockIdx.x >> 2;
+  // the workgroups of a key stream on the die whose L2 its split workgroups
+  // wrote the partials through (the split kernels group a stream's splits
+  // the same way)
+  const int bidx = xcd_grouped_block(blockIdx.x, gridDim.x);
+  const int gr = bidx >> 2;
   const int g = gr / a.row_blocks;
   const int rb = gr % a.row_blocks;
-  const int blk = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
+  const int blk = 4 * (bidx & 3) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
   const int row = rb * 32 + n;
