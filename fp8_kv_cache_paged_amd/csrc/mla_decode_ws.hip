@@ -585,8 +585,11 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // the problem read row 0 and stage zero codes
     const int qrl = 16 * e + (lane >> 2), qq = lane & 3;
     const bool q_ok = rg * (kSWaves * 32) + qrl < a.rows;
+    // a wave none of whose rows exist (a 16-head sparse token uses one of the
+    // eight) stages zeros without loading or quantizing anything
+    const bool q_any = rg * (kSWaves * 32) + 16 * e < a.rows;
     i32x4 qraw[16];
-    {
+    if (q_any) {
       const uint16_t* qsrc = q + (q_ok ? ((long)g * a.rows + rg * (kSWaves * 32) + qrl) * D : 0) + 8 * qq;
 #pragma unroll
       for (int i = 0; i < 16; ++i) qraw[i] = *reinterpret_cast<const i32x4*>(qsrc + 32 * i);
@@ -640,7 +643,8 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     }
     {
       uint2 codes[16];
-      const int qe = quantize_q_quad(qraw, codes);
+      int qe = 0;
+      if (q_any) qe = quantize_q_quad(qraw, codes);
       const int nn = qrl & 31;
       uint8_t* dst = qstage(qrl >> 5) + nn * 512 + 8 * (qq & 1);
 #pragma unroll
