@@ -359,9 +359,7 @@ def main():
     gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     mfma_peak = FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS
     if args.dot == "fp8":
-        # the role-split kernel: dense with >= 3 row blocks, any sparse shape, any fnuz cache
-        ws_path = idx is not None or (w.s_q * w.h_q + 31) // 32 >= 3 or args.kv_encoding == "e4m3fnuz"
-        kernel_name = "mla_decode_ws_kernel" if ws_path else "mla_decode_kernel"
+        kernel_name = "mla_decode_ws_kernel"   # every fp8-dot decode
     else:
         kernel_name = "mla_decode_kernel or mla_decode_rows_kernel"
     roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,

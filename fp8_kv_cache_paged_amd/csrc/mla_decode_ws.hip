@@ -875,14 +875,12 @@ hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table,
   return hipGetLastError();
 }
 
+// Every fp8-dot decode runs here, at any row count: row blocks past the
+// problem skip their work, and a one- or two-wave workgroup (the dv-split
+// kernel, kept as a test variant) is slower even for a single 16-head token
+// (tiny decode 17.5 -> 10 us). The variant flags select the other kernels.
 bool decode_ws_eligible(const DecodeLaunch& d) {
-  if (d.dot != DOT_FP8 || d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
-  // sparse: at any row count (a one-wave workgroup per 16-head token is the
-  // alternative); an fnuz cache with fp8 dots runs here at any row count (the
-  // only kernel that reads it with fp8 dots; per-token fnuz is refused
-  // earlier); dense otherwise from three row blocks up
-  if (d.topk != 0) return true;
-  return d.fnuz || d.row_blocks >= 3;
+  return d.dot == DOT_FP8 && !d.rows_kernel && !d.dv_split_kernel && !d.gather_v;
 }
 
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
