@@ -187,8 +187,13 @@ int32_t decode_impl(const mla_params* p, const void* q, const void* kv_cache, co
   d.dv_split_kernel = (variant & MLA_VARIANT_DV_SPLIT) != 0;
   d.per_token = p->kv_scale_per_token != 0;
   d.fnuz = p->kv_dtype == MLA_KV_FP8_E4M3FNUZ;
-  const char* dbg = getenv("MLA_FP8_DEBUG");
-  d.debug_print = dbg != nullptr && dbg[0] == '1';
+  // read once per process (the split-count override, read per call, is meant
+  // to be changed between calls; the plan print is not)
+  static const bool debug_print = [] {
+    const char* dbg = getenv("MLA_FP8_DEBUG");
+    return dbg != nullptr && dbg[0] == '1';
+  }();
+  d.debug_print = debug_print;
   if (d.debug_print)
     fprintf(stderr, "[mla_fp8] plan: groups=%d rows=%d splits=%d workspace=%zu cus=%d\n", d.groups, d.rows, splits,
             need, cus);
