@@ -361,7 +361,7 @@ def main():
     if args.dot == "fp8":
         kernel_name = "mla_decode_ws_kernel"   # every fp8-dot decode
     else:
-        kernel_name = "mla_decode_kernel or mla_decode_rows_kernel"
+        kernel_name = "mla_decode_rows_kernel"   # every bf16-dot decode
     roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,
                 "flop_per_launch": flops, "timing": f"{args.steps} back-to-back launches between one event pair"}
     if kern_ms > ms_per_step * 1.02:

@@ -1467,8 +1467,9 @@ static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t s
   return hipGetLastError();
 }
 
-// fp8 dots run the dv-split kernel (or, on request, the row-block one);
-// bf16 dots the row-block kernel.
+// fp8 dots run the role-split kernel; the dv-split and row-block kernels
+// serve them only when a variant flag asks for one. bf16 dots run the
+// row-block kernel.
 template <int DOT, int ROPE, bool SPARSE>
 static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   if constexpr (DOT == DOT_FP8) {
