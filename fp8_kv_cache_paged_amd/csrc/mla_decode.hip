@@ -1282,14 +1282,29 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MLA_KERNEL_PTRS, KDims
   const float inv = W > 0.f ? (a.per_token ? 1.f : *v_scale) / W : 0.f;   // per token: the row scales
   const long qrow_idx = (long)g * a.rows + row;
   uint16_t* orow = out + qrow_idx * kNope;
+  // lane half h holds dv 8 j + 4 h .. + 3 (j = 0..3) of the block's 32; one
+  // lane swap of the packed pairs gives the lower half dv 0..15 and the upper
+  // half dv 16..31, stored as two 16-byte runs per lane
+  unsigned x[4], y[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int dv = 32 * blk + 8 * j + 4 * h;
-    uint2 w;
-    w.x = bf16x2_bits(acc[4 * j] * inv, acc[4 * j + 1] * inv);
-    w.y = bf16x2_bits(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
-    *reinterpret_cast<uint2*>(orow + dv) = w;
+  for (int j = 0; j < 2; ++j) {
+    x[2 * j] = bf16x2_bits(acc[4 * j] * inv, acc[4 * j + 1] * inv);
+    x[2 * j + 1] = bf16x2_bits(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+    y[2 * j] = bf16x2_bits(acc[8 + 4 * j] * inv, acc[8 + 4 * j + 1] * inv);
+    y[2 * j + 1] = bf16x2_bits(acc[8 + 4 * j + 2] * inv, acc[8 + 4 * j + 3] * inv);
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // lower half: keeps x (dv 0-3, 8-11), takes the upper half's x into y
+    // (dv 4-7, 12-15); upper half: takes the lower half's y into x (dv 16-19,
+    // 24-27), keeps y (dv 20-23, 28-31)
+    const auto r = __builtin_amdgcn_permlane32_swap(x[k], y[k], false, false);
+    x[k] = r[0];
+    y[k] = r[1];
+  }
+  i32x4* dst = reinterpret_cast<i32x4*>(orow + 32 * blk + 16 * h);
+  dst[0] = i32x4{(int)x[0], (int)x[1], (int)y[0], (int)y[1]};
+  dst[1] = i32x4{(int)x[2], (int)x[3], (int)y[2], (int)y[3]};
   if (blk == 0 && h == 0) lse[qrow_idx] = (W > 0.f) ? (M + log2f(W)) * kLn2 : -INFINITY;
 }
 
