@@ -358,10 +358,14 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     gbps = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     mfma_peak = FP8_PEAK_TFLOPS if args.dot == "fp8" else BF16_PEAK_TFLOPS
-    if args.dot == "fp8":
-        kernel_name = "mla_decode_ws_kernel"   # every fp8-dot decode
+    # every fp8-dot decode runs the role-split kernel; bf16-dot decodes too
+    # (two-term operands) with at most 16 rows per key stream and an e4m3fn
+    # cache, the others the row-block kernel
+    rows = w.h_q if w.topk else w.s_q * w.h_q
+    if args.dot == "fp8" or (rows <= 16 and args.kv_encoding == "e4m3fn"):
+        kernel_name = "mla_decode_ws_kernel"
     else:
-        kernel_name = "mla_decode_rows_kernel"   # every bf16-dot decode
+        kernel_name = "mla_decode_rows_kernel"
     roofline = {"kernel": kernel_name, "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": kern_bytes,
                 "flop_per_launch": flops, "timing": f"{args.steps} back-to-back launches between one event pair"}
     if kern_ms > ms_per_step * 1.02:

@@ -1484,11 +1484,12 @@ static hipError_t launch_nw(const DecodeLaunch& d, const KDims& a, hipStream_t s
 
 // fp8 dots run the role-split kernel; the dv-split and row-block kernels
 // serve them only when a variant flag asks for one. bf16 dots run the
-// row-block kernel.
+// row-block kernel, or the role-split kernel's two-term form for at most 16
+// rows per key stream (decode_ws_eligible).
 template <int DOT, int ROPE, bool SPARSE>
 static hipError_t launch_gv(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
+  if (decode_ws_eligible(d)) return launch_decode_ws(d, a, st);
   if constexpr (DOT == DOT_FP8) {
-    if (decode_ws_eligible(d)) return launch_decode_ws(d, a, st);
     if (d.per_token) {
       const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
       switch (waves_per_group(d.row_blocks)) {

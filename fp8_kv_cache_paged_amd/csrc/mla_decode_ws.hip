@@ -228,13 +228,16 @@ __device__ inline void ws_fnuz_to_ocp_slice(uint8_t* lds, int bufi, int e) {
   }
 }
 
-template <int ROPE, bool FNUZ, bool SPARSE, bool PT>
+template <int ROPE, bool FNUZ, bool SPARSE, bool PT, bool SPLITQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(3, 3)))
 void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
   constexpr int D = kNope + ROPE;   // q row length
   constexpr long RB = kNope + 2 * ROPE;
   constexpr int kSpBytes = SPARSE ? kSpSlots * kSpSlotBytes : 0;
   constexpr int kPtBytes = PT ? kBufs * 512 : 0;   // per ring slot: 64 k-scales, 64 v-scales
+  // lazy-max threshold and P scale (log2) of the single-term and two-term P
+  constexpr float kTau = SPLITQ ? SoftSplit::tau : Soft<DOT_FP8>::tau;
+  constexpr float kPsLog2 = SPLITQ ? SoftSplit::ps_log2 : Soft<DOT_FP8>::ps_log2;
   static_assert(WsQ<ROPE>::lds_bytes + kSpBytes + kPtBytes <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes + kSpBytes + kPtBytes];
   uint8_t* const lds = lds_;
@@ -292,7 +295,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // ======================= S-wave: S^T, softmax, P^T ========================
     const int rb = rg * kSWaves + wave;
     const bool wave_active = rb < a.row_blocks;
-    const int row = rb * 32 + n;
+    // two-term query (SPLITQ, at most 16 rows): columns n and n + 16 of the
+    // block hold the two terms of row n, so both lane halves take row n % 16
+    const int row = rb * 32 + (SPLITQ ? (n & 15) : n);
     const bool row_ok = row < a.rows;
     const long qrow_idx = (long)g * a.rows + row;
     const bool q_ok = row_ok && wave_active;
@@ -315,7 +320,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       for (int t = 0; t < 4; ++t) {
         i32x4 v = qr_raw[t];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) v[d] = q_ok ? v[d] : 0;
+        for (int d = 0; d < 4; ++d) v[d] = q_ok && !(SPLITQ && n >= 16) ? v[d] : 0;   // rope: first term only
         qr[t] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -447,6 +452,18 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         scale_by_k(acc[0], 0, pt_base + buf * 128, 1.f);
         scale_by_k(acc[1], 1, pt_base + buf * 128, 1.f);
       }
+      if constexpr (SPLITQ) {
+        // S = S1 + S2 / 16 from columns n and n + 16 (16-lane rows 2i and
+        // 2i + 1), left in both so that both halves run the same softmax
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned u = __float_as_uint(acc[kb][r]);
+            const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            acc[kb][r] = fmaf(__uint_as_float(t[1]), 0.0625f, __uint_as_float(t[0]));
+          }
+      }
 
       // ---- mask + online softmax (log2 domain), P^T to LDS ----------------------
       const bool page_ok = page_valid(page_cur);
@@ -509,7 +526,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           inv_vrun = 1.f / vm;
         }
       }
-      const bool raise = mx > m_run + Soft<DOT_FP8>::tau;
+      const bool raise = mx > m_run + kTau;
       bool flagged = false;
       if (__ballot(raise) || vraise) {
         const float m_new = raise ? mx : m_run;
@@ -526,7 +543,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         }
         m_run = m_new;
       }
-      const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - Soft<DOT_FP8>::ps_log2;
+      const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - kPsLog2;
       float psum = 0.f;
       i32x8 pb;
       const int hv = fresh_lane() >> 5;
@@ -548,6 +565,14 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           for (int r = 0; r < 4; ++r) pe[r] = pe[r] > 0.f ? pe[r] * (v4[r] * inv_vrun) : 0.f;
         }
         pb[q4] = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
+        if constexpr (SPLITQ) {
+          // columns n + 16 carry the second term of P: 16 (p - e4m3fn(p))
+          float c1[4];
+          fp8x4_to_f32(pb[q4], c1);
+          const int c2 = f32x4_to_fp8x4(16.f * (pe[0] - c1[0]), 16.f * (pe[1] - c1[1]), 16.f * (pe[2] - c1[2]),
+                                        16.f * (pe[3] - c1[3]));
+          pb[q4] = (fresh_lane() & 16) ? c2 : pb[q4];
+        }
       }
       l_run += psum;
       const int lp = fresh_lane();
@@ -566,9 +591,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // v_scale, or the per-row v_run stored beside the lse)
     if (h == 0) xfin[wave * 32 + n] = nonempty ? (a.splits == 1 ? (PT ? v_run : *v_scale) : 1.f) / l_tot : 0.f;
     if (wave_active && h == 0) {
-      const float lse2 = nonempty ? m_run + log2f(l_tot) - Soft<DOT_FP8>::ps_log2 : -INFINITY;
+      const float lse2 = nonempty ? m_run + log2f(l_tot) - kPsLog2 : -INFINITY;
       if (a.splits == 1) {
-        if (row_ok) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
+        if (row_ok && !(SPLITQ && n >= 16)) lse[qrow_idx] = nonempty ? lse2 * kLn2 : -INFINITY;
       } else {
         const long prow = (((long)s * a.groups + g) * a.row_blocks + rb) * 32 + n;
         part_lse[prow] = lse2;
@@ -584,13 +609,17 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // group, one per lane quad (quarter qq holds chunks 4 i + qq); rows outside
     // the problem read row 0 and stage zero codes
     const int qrl = 16 * e + (lane >> 2), qq = lane & 3;
-    const bool q_ok = rg * (kSWaves * 32) + qrl < a.rows;
+    // two-term query (SPLITQ): wave 1 stages the second terms of rows 0..15
+    // as rows 16..31 of the block
+    const bool q_second = SPLITQ && e == 1;
+    const int qsrow = q_second ? qrl - 16 : qrl;   // the query row this lane reads
+    const bool q_ok = rg * (kSWaves * 32) + qsrow < a.rows;
     // a wave none of whose rows exist (a 16-head sparse token uses one of the
     // eight) stages zeros without loading or quantizing anything
-    const bool q_any = rg * (kSWaves * 32) + 16 * e < a.rows;
+    const bool q_any = rg * (kSWaves * 32) + (q_second ? 0 : 16 * e) < a.rows;
     i32x4 qraw[16];
     if (q_any) {
-      const uint16_t* qsrc = q + (q_ok ? ((long)g * a.rows + rg * (kSWaves * 32) + qrl) * D : 0) + 8 * qq;
+      const uint16_t* qsrc = q + (q_ok ? ((long)g * a.rows + rg * (kSWaves * 32) + qsrow) * D : 0) + 8 * qq;
 #pragma unroll
       for (int i = 0; i < 16; ++i) qraw[i] = *reinterpret_cast<const i32x4*>(qsrc + 32 * i);
     }
@@ -644,7 +673,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     {
       uint2 codes[16];
       int qe = 0;
-      if (q_any) qe = quantize_q_quad(qraw, codes);
+      if (q_any) qe = q_second ? quantize_q_quad_residual(qraw, codes) : quantize_q_quad(qraw, codes);
       const int nn = qrl & 31;
       uint8_t* dst = qstage(qrl >> 5) + nn * 512 + 8 * (qq & 1);
 #pragma unroll
@@ -790,6 +819,17 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // ---- epilogue ----------------------------------------------------------------------
     __syncthreads();   // the S-waves' per-row scales are in LDS
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last P.V MFMAs done
+    if constexpr (SPLITQ) {
+      // O = O1 + O2 / 16 from columns n and n + 16 (row block 0 only)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const unsigned u = __float_as_uint(O[j][0][x]);
+          const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+          O[j][0][x] = fmaf(__uint_as_float(t[1]), 0.0625f, __uint_as_float(t[0]));
+        }
+    }
     // O^T register x of block (j, r): dv 32 (2e + j) + 8 (x / 4) + 4 h + x % 4, row 32 rbr + n
 #pragma unroll
     for (int r = 0; r < kSWaves; ++r) {
@@ -878,32 +918,41 @@ hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table,
 // Every fp8-dot decode runs here, at any row count: row blocks past the
 // problem skip their work, and a one- or two-wave workgroup (the dv-split
 // kernel, kept as a test variant) is slower even for a single 16-head token
-// (tiny decode 17.5 -> 10 us). The variant flags select the other kernels.
+// (tiny decode 17.5 -> 10 us). bf16-dot decodes of at most 16 rows per key
+// stream (a 16-head sparse token, a small dense decode) run here too, on the
+// two-term operands (SPLITQ) in the half row block the rows leave free; an
+// e4m3fnuz cache keeps them on the row-block kernel, which reads its codes
+// exactly. The variant flags select the other kernels.
 bool decode_ws_eligible(const DecodeLaunch& d) {
-  return d.dot == DOT_FP8 && !d.rows_kernel && !d.dv_split_kernel && !d.gather_v;
+  if (d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
+  return d.dot == DOT_FP8 || (d.rows <= 16 && !d.fnuz);
 }
 
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
 #define MLA_WS_ARGS d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
-#define MLA_WS_LAUNCH(R, F, S, P) \
-  hipLaunchKernelGGL((mla_decode_ws_kernel<R, F, S, P>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a)
-  const bool r64 = d.d_rope == 64;
-  if (d.topk != 0) {
-    if (d.per_token) {
-      if (r64) MLA_WS_LAUNCH(64, false, true, true); else MLA_WS_LAUNCH(0, false, true, true);
-    } else if (d.fnuz) {
-      if (r64) MLA_WS_LAUNCH(64, true, true, false); else MLA_WS_LAUNCH(0, true, true, false);
+#define MLA_WS_LAUNCH(R, F, S, P, Q) \
+  hipLaunchKernelGGL((mla_decode_ws_kernel<R, F, S, P, Q>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a)
+#define MLA_WS_ROPE(F, S, P, Q) \
+  if (d.d_rope == 64) MLA_WS_LAUNCH(64, F, S, P, Q); else MLA_WS_LAUNCH(0, F, S, P, Q)
+  if (d.dot != DOT_FP8) {   // bf16 dots, at most 16 rows, no fnuz
+    if (d.topk != 0) {
+      if (d.per_token) { MLA_WS_ROPE(false, true, true, true); } else { MLA_WS_ROPE(false, true, false, true); }
     } else {
-      if (r64) MLA_WS_LAUNCH(64, false, true, false); else MLA_WS_LAUNCH(0, false, true, false);
+      if (d.per_token) { MLA_WS_ROPE(false, false, true, true); } else { MLA_WS_ROPE(false, false, false, true); }
     }
+  } else if (d.topk != 0) {
+    if (d.per_token) { MLA_WS_ROPE(false, true, true, false); }
+    else if (d.fnuz) { MLA_WS_ROPE(true, true, false, false); }
+    else { MLA_WS_ROPE(false, true, false, false); }
   } else if (d.per_token) {
-    if (r64) MLA_WS_LAUNCH(64, false, false, true); else MLA_WS_LAUNCH(0, false, false, true);
+    MLA_WS_ROPE(false, false, true, false);
   } else if (d.fnuz) {
-    if (r64) MLA_WS_LAUNCH(64, true, false, false); else MLA_WS_LAUNCH(0, true, false, false);
+    MLA_WS_ROPE(true, false, false, false);
   } else {
-    if (r64) MLA_WS_LAUNCH(64, false, false, false); else MLA_WS_LAUNCH(0, false, false, false);
+    MLA_WS_ROPE(false, false, false, false);
   }
+#undef MLA_WS_ROPE
 #undef MLA_WS_LAUNCH
 #undef MLA_WS_ARGS
   return hipGetLastError();

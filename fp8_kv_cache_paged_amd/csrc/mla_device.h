@@ -746,6 +746,42 @@ __device__ inline int quantize_q_quad(const i32x4 raw[16], uint2 codes[16]) {
   return e;
 }
 
+// Second term of the two-term query that gives bf16-dot accuracy on the fp8
+// matrix cores (the role-split kernel with bf16 dots, at most 16 rows per key
+// stream). With x = q * 2^-e (the exponent quantize_q_quad takes) and
+// c1 = e4m3fn(x) its codes, these are the codes of c2 = 16 (x - c1). x has at
+// most 8 significant bits (a bf16 value times a power of two) and c1 keeps
+// the top 4 with rounding, so x - c1 has at most 4 and, whenever x is a
+// normal e4m3fn magnitude (>= 2^-6), c2 is exact: 2^e (c1 + c2 / 16) = q.
+// Below 2^-6 (under 2^-6 / 448 of the row's largest value) the residual is
+// rounded to e4m3fn's subnormal grid. Returns the exponent e.
+__device__ inline int quantize_q_quad_residual(const i32x4 raw[16], uint2 codes[16]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo((unsigned)raw[i][d])), fabsf(bf16_hi((unsigned)raw[i][d]))));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = q_exponent(amax);
+  const int ne = -e;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const unsigned wa = (unsigned)raw[i][2 * half], wb = (unsigned)raw[i][2 * half + 1];
+      float x[4] = {ldexpf(bf16_lo(wa), ne), ldexpf(bf16_hi(wa), ne), ldexpf(bf16_lo(wb), ne), ldexpf(bf16_hi(wb), ne)};
+      float c1[4];
+      fp8x4_to_f32(f32x4_to_fp8x4(x[0], x[1], x[2], x[3]), c1);
+      const unsigned c2 = (unsigned)f32x4_to_fp8x4(16.f * (x[0] - c1[0]), 16.f * (x[1] - c1[1]),
+                                                   16.f * (x[2] - c1[2]), 16.f * (x[3] - c1[3]));
+      if (half == 0) codes[i].x = c2; else codes[i].y = c2;
+    }
+  }
+  return e;
+}
+
 // gfx942's e4m3fnuz codes turned into OCP e4m3fn codes of the same value,
 // in place in this wave's 4 KiB slice of a landed tile (the fp8 matrix cores
 // read OCP codes only). A code whose exponent field is 2 or more is the OCP
@@ -765,8 +801,8 @@ __device__ inline unsigned fnuz4_to_ocp4(unsigned x) {
   return (x & 0x80808080u) | (rb & bm) | (rs & ~bm);
 }
 
-// The role-split decode (mla_decode_ws.hip): fp8 dots, per-tensor scales,
-// dense, three or more 32-row blocks per key stream.
+// The role-split decode (mla_decode_ws.hip): every fp8-dot decode, and
+// bf16-dot decodes of at most 16 rows per key stream (two-term operands).
 bool decode_ws_eligible(const DecodeLaunch& d);
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st);
 
@@ -785,5 +821,10 @@ template <int DOT> struct Soft;
 #endif
 template <> struct Soft<1> { static constexpr float tau = MLA_FP8_TAU, ps_log2 = 8 - MLA_FP8_TAU; };
 template <> struct Soft<0> { static constexpr float tau = 8.f, ps_log2 = 0.f; };
+// The two-term P of the role-split kernel's bf16-dot form (p = c1 + c2 / 16,
+// both e4m3fn) keeps about 8 bits only while c1 is normal: tau = 0 and
+// 2^8 of scale put that down to 2^-14 below the running max (the single
+// term's 2^-11, one binade more than a bf16 P needs for a tail at e^-9).
+struct SoftSplit { static constexpr float tau = 0.f, ps_log2 = 8.f; };
 
 }  // namespace mla

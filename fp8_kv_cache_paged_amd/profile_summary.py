@@ -127,15 +127,16 @@ def per_config(pairs, out_path, commands, counters=None):
     lines += ["commands (run from /tmp with TMPDIR=/tmp; repository at /root/repo):"]
     lines += [f"  {c}" for c in commands]
     lines += ["", f"source_sha256: {source_sha256()}", "",
-              f"  {'workload':<14} {'split kernel us':>16} {'calls':>6} {'combine us':>11} {'calls':>6}"]
+              f"  {'workload':<14} {'split kernel us':>16} {'calls':>6} {'combine us':>11} {'calls':>6}  split kernel"]
     for pair in pairs:
         name, d = pair.split("=", 1)
         st = kernel_stats(d)
-        sk = [(c, a) for n, c, a, _ in st if n.startswith("void mla::mla_decode")]
+        sk = [(c, a, n.split("<")[0].replace("void mla::", "")) for n, c, a, _ in st
+              if n.startswith("void mla::mla_decode")]
         ck = [(c, a) for n, c, a, _ in st if "mla_combine_kernel" in n]
-        s_c, s_a = max(sk) if sk else (0, 0.0)
+        s_c, s_a, s_n = max(sk) if sk else (0, 0.0, "-")
         c_c, c_a = max(ck) if ck else (0, 0.0)
-        lines.append(f"  {name:<14} {s_a / 1e3:>16.2f} {s_c:>6} {c_a / 1e3:>11.2f} {c_c:>6}")
+        lines.append(f"  {name:<14} {s_a / 1e3:>16.2f} {s_c:>6} {c_a / 1e3:>11.2f} {c_c:>6}  {s_n}")
     if counters:
         lines += per_config_counters(counters)
     os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
