@@ -228,16 +228,20 @@ __device__ inline void ws_fnuz_to_ocp_slice(uint8_t* lds, int bufi, int e) {
   }
 }
 
-template <int ROPE, bool FNUZ, bool SPARSE, bool PT, bool SPLITQ>
+// TT: 0 one-term query and P; 1 (at most 16 rows, fp8 dots) two-term query,
+// one-term P; 2 (at most 16 rows, bf16 dots) two-term query and P.
+template <int ROPE, bool FNUZ, bool SPARSE, bool PT, int TT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads), amdgpu_waves_per_eu(3, 3)))
 void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
+  constexpr bool SPLITQ = TT >= 1;   // columns n + 16 carry the second query term
+  constexpr bool SPLITP = TT == 2;   // ... and the second term of P
   constexpr int D = kNope + ROPE;   // q row length
   constexpr long RB = kNope + 2 * ROPE;
   constexpr int kSpBytes = SPARSE ? kSpSlots * kSpSlotBytes : 0;
   constexpr int kPtBytes = PT ? kBufs * 512 : 0;   // per ring slot: 64 k-scales, 64 v-scales
   // lazy-max threshold and P scale (log2) of the single-term and two-term P
-  constexpr float kTau = SPLITQ ? SoftSplit::tau : Soft<DOT_FP8>::tau;
-  constexpr float kPsLog2 = SPLITQ ? SoftSplit::ps_log2 : Soft<DOT_FP8>::ps_log2;
+  constexpr float kTau = SPLITP ? SoftSplit::tau : Soft<DOT_FP8>::tau;
+  constexpr float kPsLog2 = SPLITP ? SoftSplit::ps_log2 : Soft<DOT_FP8>::ps_log2;
   static_assert(WsQ<ROPE>::lds_bytes + kSpBytes + kPtBytes <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_[WsQ<ROPE>::lds_bytes + kSpBytes + kPtBytes];
   uint8_t* const lds = lds_;
@@ -454,14 +458,20 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       }
       if constexpr (SPLITQ) {
         // S = S1 + S2 / 16 from columns n and n + 16 (16-lane rows 2i and
-        // 2i + 1), left in both so that both halves run the same softmax
+        // 2i + 1), left in both so that both halves run the same softmax.
+        // Registers go in pairs: the swap of (r, r + 1) puts S1 and S2 of r
+        // in the even rows and those of r + 1 in the odd rows; the sum's
+        // swap with itself spreads both sums to every lane.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const unsigned u = __float_as_uint(acc[kb][r]);
-            const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-            acc[kb][r] = fmaf(__uint_as_float(t[1]), 0.0625f, __uint_as_float(t[0]));
+          for (int r = 0; r < 16; r += 2) {
+            const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[kb][r]),
+                                                            __float_as_uint(acc[kb][r + 1]), false, false);
+            const unsigned c = __float_as_uint(fmaf(__uint_as_float(t[1]), 0.0625f, __uint_as_float(t[0])));
+            const auto u = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+            acc[kb][r] = __uint_as_float(u[0]);
+            acc[kb][r + 1] = __uint_as_float(u[1]);
           }
       }
 
@@ -547,6 +557,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
       float psum = 0.f;
       i32x8 pb;
       const int hv = fresh_lane() >> 5;
+      const bool p_second = SPLITQ && (fresh_lane() & 16) != 0;   // a column n + 16 lane
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const int kb = q4 >> 2, r0 = 4 * (q4 & 3);
@@ -565,13 +576,15 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           for (int r = 0; r < 4; ++r) pe[r] = pe[r] > 0.f ? pe[r] * (v4[r] * inv_vrun) : 0.f;
         }
         pb[q4] = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
-        if constexpr (SPLITQ) {
+        if constexpr (SPLITP) {
           // columns n + 16 carry the second term of P: 16 (p - e4m3fn(p))
           float c1[4];
           fp8x4_to_f32(pb[q4], c1);
           const int c2 = f32x4_to_fp8x4(16.f * (pe[0] - c1[0]), 16.f * (pe[1] - c1[1]), 16.f * (pe[2] - c1[2]),
                                         16.f * (pe[3] - c1[3]));
-          pb[q4] = (fresh_lane() & 16) ? c2 : pb[q4];
+          pb[q4] = p_second ? c2 : pb[q4];
+        } else if constexpr (SPLITQ) {
+          pb[q4] = p_second ? 0 : pb[q4];   // one-term P: columns n + 16 add nothing
         }
       }
       l_run += psum;
@@ -819,7 +832,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // ---- epilogue ----------------------------------------------------------------------
     __syncthreads();   // the S-waves' per-row scales are in LDS
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last P.V MFMAs done
-    if constexpr (SPLITQ) {
+    if constexpr (SPLITP) {
       // O = O1 + O2 / 16 from columns n and n + 16 (row block 0 only)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -918,11 +931,12 @@ hipError_t launch_debug_gather_ws(const uint8_t* kv, const int32_t* block_table,
 // Every fp8-dot decode runs here, at any row count: row blocks past the
 // problem skip their work, and a one- or two-wave workgroup (the dv-split
 // kernel, kept as a test variant) is slower even for a single 16-head token
-// (tiny decode 17.5 -> 10 us). bf16-dot decodes of at most 16 rows per key
-// stream (a 16-head sparse token, a small dense decode) run here too, on the
-// two-term operands (SPLITQ) in the half row block the rows leave free; an
-// e4m3fnuz cache keeps them on the row-block kernel, which reads its codes
-// exactly. The variant flags select the other kernels.
+// (tiny decode 17.5 -> 10 us). With at most 16 rows per key stream (a 16-head
+// sparse token, a small dense decode) the half row block those rows leave free
+// carries second terms: of the query (fp8 dots then multiply the exact bf16
+// query), and for bf16 dots of P too. An e4m3fnuz cache keeps bf16 dots on the
+// row-block kernel, which reads its codes exactly. The variant flags select
+// the other kernels.
 bool decode_ws_eligible(const DecodeLaunch& d) {
   if (d.rows_kernel || d.dv_split_kernel || d.gather_v) return false;
   return d.dot == DOT_FP8 || (d.rows <= 16 && !d.fnuz);
@@ -931,27 +945,34 @@ bool decode_ws_eligible(const DecodeLaunch& d) {
 hipError_t launch_decode_ws(const DecodeLaunch& d, const KDims& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.groups * a.splits * a.row_groups));
 #define MLA_WS_ARGS d.q, d.kv, d.block_table, d.seq_lens, d.indices, d.k_scale, d.v_scale, d.out, d.lse, d.part_o, d.part_lse
-#define MLA_WS_LAUNCH(R, F, S, P, Q) \
-  hipLaunchKernelGGL((mla_decode_ws_kernel<R, F, S, P, Q>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a)
-#define MLA_WS_ROPE(F, S, P, Q) \
-  if (d.d_rope == 64) MLA_WS_LAUNCH(64, F, S, P, Q); else MLA_WS_LAUNCH(0, F, S, P, Q)
+#define MLA_WS_LAUNCH(R, F, S, P, T) \
+  hipLaunchKernelGGL((mla_decode_ws_kernel<R, F, S, P, T>), grid, dim3(kWsThreads), 0, st, MLA_WS_ARGS, a)
+#define MLA_WS_ROPE(F, S, P, T) \
+  if (d.d_rope == 64) MLA_WS_LAUNCH(64, F, S, P, T); else MLA_WS_LAUNCH(0, F, S, P, T)
+#define MLA_WS_FP8(T)                                          \
+  if (d.topk != 0) {                                           \
+    if (d.per_token) { MLA_WS_ROPE(false, true, true, T); }    \
+    else if (d.fnuz) { MLA_WS_ROPE(true, true, false, T); }    \
+    else { MLA_WS_ROPE(false, true, false, T); }               \
+  } else if (d.per_token) {                                    \
+    MLA_WS_ROPE(false, false, true, T);                        \
+  } else if (d.fnuz) {                                         \
+    MLA_WS_ROPE(true, false, false, T);                        \
+  } else {                                                     \
+    MLA_WS_ROPE(false, false, false, T);                       \
+  }
   if (d.dot != DOT_FP8) {   // bf16 dots, at most 16 rows, no fnuz
     if (d.topk != 0) {
-      if (d.per_token) { MLA_WS_ROPE(false, true, true, true); } else { MLA_WS_ROPE(false, true, false, true); }
+      if (d.per_token) { MLA_WS_ROPE(false, true, true, 2); } else { MLA_WS_ROPE(false, true, false, 2); }
     } else {
-      if (d.per_token) { MLA_WS_ROPE(false, false, true, true); } else { MLA_WS_ROPE(false, false, false, true); }
+      if (d.per_token) { MLA_WS_ROPE(false, false, true, 2); } else { MLA_WS_ROPE(false, false, false, 2); }
     }
-  } else if (d.topk != 0) {
-    if (d.per_token) { MLA_WS_ROPE(false, true, true, false); }
-    else if (d.fnuz) { MLA_WS_ROPE(true, true, false, false); }
-    else { MLA_WS_ROPE(false, true, false, false); }
-  } else if (d.per_token) {
-    MLA_WS_ROPE(false, false, true, false);
-  } else if (d.fnuz) {
-    MLA_WS_ROPE(true, false, false, false);
+  } else if (d.rows <= 16) {
+    MLA_WS_FP8(1)
   } else {
-    MLA_WS_ROPE(false, false, false, false);
+    MLA_WS_FP8(0)
   }
+#undef MLA_WS_FP8
 #undef MLA_WS_ROPE
 #undef MLA_WS_LAUNCH
 #undef MLA_WS_ARGS

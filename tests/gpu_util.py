@@ -9,7 +9,11 @@ compared with the oracle evaluated at the kernel's quantized query Q' (the
 quantization itself is checked bit-exactly elsewhere), and `out` with the
 oracle at the exact bf16 query. The lse difference from the oracle at the
 exact bf16 query is reported beside it (for fp8 dots it is the effect of
-quantizing Q and exceeds 1e-3 on short or peaky rows).
+quantizing Q and exceeds 1e-3 on short or peaky rows). With at most 16 query
+rows per key stream the kernel multiplies the exact bf16 query in both dot
+modes (its second term rides in the half row block the rows leave free), and
+the plain oracle is the reference for lse and rows there too
+(kernel_query_exact).
 
 Beside the whole-tensor figure every query row (b, i, h) is held to its own
 relative L2 error against the oracle at the query the kernel multiplies (Q'
@@ -57,6 +61,14 @@ def run(w, t, dot, num_splits=None, **kw):
                           causal=w.causal, indices=t["idx"], softmax_scale=w.softmax_scale or 0.0, **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def kernel_query_exact(w, dot):
+    """Whether the default decode multiplies the exact bf16 query: bf16 dots,
+    or at most 16 rows per key stream (the role-split kernel's two-term query;
+    the variant kernels always quantize it for fp8 dots)."""
+    rows = w.h_q if w.indices is not None else w.s_q * w.h_q
+    return dot == "bf16" or rows <= 16
 
 
 def oracle(w, q_prime=False):
@@ -132,5 +144,5 @@ def check(w, oc, dot, num_splits=None, t=None, **kw):
     t = device_inputs(w) if t is None else t
     out, lse = run(w, t, dot, num_splits, **kw)
     ref_o, ref_l = oc.exact
-    ref_q = oc.qprime if dot == "fp8" else oc.exact
+    ref_q = oc.exact if kernel_query_exact(w, dot) else oc.qprime
     return compare(out, lse, ref_o, ref_l, ref_q[1], dot, ref_out_rows=ref_q[0])

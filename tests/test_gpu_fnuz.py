@@ -106,7 +106,8 @@ def test_fnuz_parity_fp8_dots(idx, splits):
     # against the oracle on the cache as the fp8 path reads it
     out, lse = gu.run(w, t, "fp8", num_splits=splits)
     oc2 = gu.OracleCache(_transcoded(w))
-    res2 = gu.compare(out, lse, *oc2.exact, oc2.qprime[1], "fp8", ref_out_rows=oc2.qprime[0])
+    rq = oc2.exact if gu.kernel_query_exact(w, "fp8") else oc2.qprime
+    res2 = gu.compare(out, lse, *oc2.exact, rq[1], "fp8", ref_out_rows=rq[0])
     print(f"fnuz fp8 dots {name}{kw} splits={splits}: vs exact fnuz {res}; vs the transcoded cache {res2}")
 
 
@@ -124,7 +125,8 @@ def test_fnuz_nan_code_reads_as_zero_fp8_dots():
     out, lse = gu.run(w, t, "fp8", num_splits=1)
     w.kv_cache[page, 5, 17] = 0x00
     oc = gu.OracleCache(_transcoded(w))
-    gu.compare(out, lse, *oc.exact, oc.qprime[1], "fp8", ref_out_rows=oc.qprime[0])
+    rq = oc.exact if gu.kernel_query_exact(w, "fp8") else oc.qprime
+    gu.compare(out, lse, *oc.exact, rq[1], "fp8", ref_out_rows=rq[0])
 
 
 def test_fnuz_full_sparse_configuration_fp8_dots():

@@ -202,7 +202,7 @@ def test_sparse_prefill_16k_tokens(dot):
     ws.q_bits = w.q_bits[:, tok]
     ws.indices = w.indices[:, tok]
     oc = gu.OracleCache(ws)
-    ref_q = oc.qprime if dot == "fp8" else oc.exact
+    ref_q = oc.exact if gu.kernel_query_exact(w, dot) else oc.qprime
     res = gu.compare(out[:, tok], lse[:, tok], *oc.exact, ref_q[1], dot, ref_out_rows=ref_q[0])
     print(f"sparse prefill 16K, {dot} dots, {len(tok)} sampled tokens: {res}")
 

@@ -44,7 +44,7 @@ def _check(w, ks, vs, splits, dot="fp8"):
     kw = dict(d_nope=w.d_nope, d_rope=w.d_rope, causal=w.causal, softmax_scale=w.softmax_scale,
               indices=w.indices)
     ref_o, ref_l = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, **kw)
-    if dot == "fp8":
+    if not gu.kernel_query_exact(w, dot):
         qp = attn.dequantized_q_nope(w.q_bits)
         ref_oq, ref_lq = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs,
                                          q_nope_override=qp, **kw)

@@ -96,7 +96,7 @@ def test_sweep_matches_oracle(case):
     out = out.float().cpu().numpy().astype(np.float64)
     lse = lse.cpu().numpy().astype(np.float64)
     ref_o, ref_l = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs, **ka)
-    if dot == "fp8":
+    if not gu.kernel_query_exact(w, dot):
         qp = attn.dequantized_q_nope(w.q_bits, w.d_nope)
         ref_oq, ref_lq = attn.mla_decode(w.q_bits, w.kv_cache, w.block_table, w.seq_lens, ks, vs,
                                          q_nope_override=qp, **ka)

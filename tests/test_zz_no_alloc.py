@@ -36,7 +36,7 @@ def _both(w, t, dot, num_splits):
 def _against_oracle(w, out, lse, dot):
     oc = gu.OracleCache(w)
     ref_o, ref_l = oc.exact
-    ref_q = oc.qprime if dot == "fp8" else oc.exact
+    ref_q = oc.exact if gu.kernel_query_exact(w, dot) else oc.qprime
     return gu.compare(out, lse, ref_o, ref_l, ref_q[1], dot, ref_out_rows=ref_q[0])
 
 
