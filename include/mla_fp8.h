@@ -40,13 +40,14 @@
  *   it by more than 3 in log2 units (so p <= 8), to e4m3fn after scaling it
  *   by 32 (values <= 256); MLA_DOT_BF16 keeps Q in bf16 and
  *   converts the cache bytes to bf16 exactly. With at most 16 query rows per
- *   key stream (s_q * h_q dense, h_q sparse) and an e4m3fn cache, MLA_DOT_BF16
- *   forms the same products on the fp8 matrix cores from two-term operands:
- *   each query row's nope part as 2^e (c1 + c2 / 16), c1 and c2 e4m3fn codes,
- *   which equals the bf16 query for every element of magnitude >= 2^(e-6)
- *   (e as for MLA_DOT_FP8), and P as c1 + c2 / 16 with c1 = e4m3fn(p), about
- *   8 significant bits (as a bf16 P) for p down to 2^-14 of the running max,
- *   which is then raised at every larger tile max, with P scaled by 256.
+ *   key stream (s_q * h_q dense, h_q sparse) both modes multiply the exact
+ *   bf16 query, on the fp8 matrix cores, as two terms: each row's nope part
+ *   as 2^e (c1 + c2 / 16), c1 and c2 e4m3fn codes, equal to the bf16 query
+ *   for every element of magnitude >= 2^(e-6) (e as above). MLA_DOT_FP8 then
+ *   packs P as above; MLA_DOT_BF16 (e4m3fn cache) packs P as two terms too,
+ *   c1 + c2 / 16 with c1 = e4m3fn(p), about 8 significant bits (as a bf16 P)
+ *   for p down to 2^-14 of the running max, which is then raised at every
+ *   larger tile max, with P scaled by 256.
  *
  * Ownership, streams and threads: the library never allocates, frees or
  * synchronizes device memory, apart from one fixed device array per GPU that
