@@ -1,4 +1,5 @@
-// FP8-dot paged MLA decode with role-split waves, three per SIMD (gfx950).
+// Paged MLA decode with role-split waves, three per SIMD (gfx950): every
+// fp8-dot decode, and bf16-dot decodes of at most 16 rows per key stream.
 //
 // What is computed is the decode of mla_decode.hip (FlashMLA PR #82 "update fp8
 // support", description; ROCm/aiter PR #6199, Technical details; InfiniCore
@@ -43,6 +44,13 @@
 // raised running max and the P scale are those of mla_decode.hip
 // (mla_device.h); the two kernels issue the same products and agree to
 // rounding order.
+//
+// Two-term forms (template TT, at most 16 query rows per key stream): the
+// rows fill only columns 0..15 of row block 0, so columns 16..31 carry a
+// second e4m3fn term, 16 (x - e4m3fn(x)), of each row's query (TT 1: fp8
+// dots multiply the exact bf16 query) and of P as well (TT 2: bf16-dot
+// accuracy on the fp8 matrix cores). The S-wave adds the column pairs after
+// its S^T products; the PV-waves fold O's column pairs once, at the end.
 
 #include "mla_device.h"
 
