@@ -364,8 +364,10 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     // Per-token scales: P is packed as p * v_j / v_run, v_run a reference
     // v-scale raised lazily (to the tile's largest when a key's v-scale
     // exceeds 1.5 v_run, so that P stays <= 1.5 * 2^8 = 384 < 448); O carries
-    // v_run and is rescaled by v_old / v_new when it rises.
-    float v_run = 0.f, inv_vrun = 0.f;
+    // v_run and is rescaled by v_old / v_new when it rises. 1 / v_run rides
+    // in the exponent (log2 v_run, 0 while v_run is), so p / v_run costs no
+    // multiply; the row sums take v_run back once per tile.
+    float v_run = 0.f;
     // k-scales of the lane's keys of key block kb (register r: key 32 kb + 8 j
     // + 4 ((j + h) & 1) + r % 4, j = r / 4), four per read
     // (one read in flight at a time: the S-wave's registers are full here)
@@ -541,7 +543,6 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           vraise = v_run > 0.f;
           vfac = vraise ? v_run / vm : 1.f;
           v_run = vm;
-          inv_vrun = 1.f / vm;
         }
       }
       const bool raise = mx > m_run + kTau;
@@ -561,7 +562,8 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         }
         m_run = m_new;
       }
-      const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - kPsLog2;
+      const float m_exp = ((m_run == -INFINITY) ? 0.f : m_run) - kPsLog2 +
+                          (PT && v_run > 0.f ? __builtin_amdgcn_logf(v_run) : 0.f);
       float psum = 0.f;
       i32x8 pb;
       const int hv = fresh_lane() >> 5;
@@ -576,12 +578,12 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           psum += pe[r];
         }
         if constexpr (PT) {
-          // p times its key's v-scale / v_run; masked keys (p = 0) skip the
-          // scale, which may be stale
+          // (p / v_run) times its key's v-scale (0 for a key that does not
+          // exist, whose p is 0 too)
           const int j = q4 & 3;
           const f32x4 v4 = *reinterpret_cast<const f32x4*>(pt_base + buf * 128 + 64 + 32 * kb + 8 * j + 4 * ((j + hv) & 1));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) pe[r] = pe[r] > 0.f ? pe[r] * (v4[r] * inv_vrun) : 0.f;
+          for (int r = 0; r < 4; ++r) pe[r] *= v4[r];
         }
         pb[q4] = f32x4_to_fp8x4(pe[0], pe[1], pe[2], pe[3]);
         if constexpr (SPLITP) {
@@ -595,7 +597,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
           pb[q4] = p_second ? 0 : pb[q4];   // one-term P: columns n + 16 add nothing
         }
       }
-      l_run += psum;
+      l_run += PT ? psum * v_run : psum;
       const int lp = fresh_lane();
       uint8_t* pdst = xp + par * WsX::p_bytes + wave * 2048 + lp * 16;
       *reinterpret_cast<i32x4*>(pdst) = i32x4{pb[0], pb[1], pb[2], pb[3]};
@@ -654,19 +656,28 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
     };
     // per-token scales of tile t (dense: its page id) into ring slot bufi:
     // the k-scales by wave 1, the v-scales by wave 2, one 4-byte-per-lane copy
-    // each (a missing page's keys are masked and its scales never read)
+    // each. Keys that do not exist (a page's slack, a missing page, a skipped
+    // sparse entry) get 0 instead of whatever the caller's array holds there,
+    // so that the S-wave's P times v-scale needs no guard (0 times 0).
     constexpr bool kPtWave = PT;
     const bool pt_wave = kPtWave && (e == 1 || e == 2);
     auto issue_pt = [&](int t, int bufi, int page) {
       if constexpr (PT) {
         if (pt_wave) {
           const float* sc = e == 1 ? k_scale : v_scale;
+          const float* zeros = reinterpret_cast<const float*>(kWsZeros);
           uint8_t* dst = reinterpret_cast<uint8_t*>(pt_base + bufi * 128 + (e == 2 ? 64 : 0));
           if constexpr (SPARSE) {
             const int cr = ws_sparse_row(sp_slot(t), fresh_lane(), sk, a.num_pages);
-            load_lds4_gather(cr >= 0 ? sc + cr : reinterpret_cast<const float*>(kWsMinusOne), dst);
-          } else if (page_valid(page)) {
-            load_lds4_row(sc + (long)page * kKeys, dst);
+            load_lds4_gather(cr >= 0 ? sc + cr : zeros, dst);
+          } else {
+            const int valid = page_valid(page) ? min(kKeys, sk - (u0 + t) * kKeys) : 0;
+            if (valid == kKeys) {
+              load_lds4_row(sc + (long)page * kKeys, dst);
+            } else {
+              const int lk = fresh_lane();
+              load_lds4_gather(lk < valid ? sc + (long)page * kKeys + lk : zeros, dst);
+            }
           }
         }
       }
