@@ -566,8 +566,9 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
                           (PT && v_run > 0.f ? __builtin_amdgcn_logf(v_run) : 0.f);
       float psum = 0.f;
       i32x8 pb;
-      const int hv = fresh_lane() >> 5;
-      const bool p_second = SPLITQ && (fresh_lane() & 16) != 0;   // a column n + 16 lane
+      const int lp = fresh_lane();
+      const int hv = lp >> 5;
+      const bool p_second = SPLITQ && (lp & 16) != 0;   // a column n + 16 lane
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const int kb = q4 >> 2, r0 = 4 * (q4 & 3);
@@ -575,7 +576,7 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pe[r] = __builtin_amdgcn_exp2f(fmaf(acc[kb][r0 + r], zscale, -m_exp));
-          psum += pe[r];
+          psum = (q4 == 0 && r == 0) ? pe[r] : psum + pe[r];
         }
         if constexpr (PT) {
           // (p / v_run) times its key's v-scale (0 for a key that does not
@@ -598,7 +599,6 @@ void mla_decode_ws_kernel(MLA_KERNEL_PTRS, KDims a) {
         }
       }
       l_run += PT ? psum * v_run : psum;
-      const int lp = fresh_lane();
       uint8_t* pdst = xp + par * WsX::p_bytes + wave * 2048 + lp * 16;
       *reinterpret_cast<i32x4*>(pdst) = i32x4{pb[0], pb[1], pb[2], pb[3]};
       *reinterpret_cast<i32x4*>(pdst + 1024) = i32x4{pb[4], pb[5], pb[6], pb[7]};
