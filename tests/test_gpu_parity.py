@@ -149,7 +149,8 @@ def test_v_scale_linearity_and_k_scale():
 FULL = [("tiny", "bf16"), ("tiny", "fp8"), ("mtp", "bf16"), ("mtp", "fp8"), ("varlen", "fp8"),
         ("large", "bf16"), ("large", "fp8"), ("sparse", "bf16"), ("sparse", "fp8"), ("metric", "fp8"),
         ("metric", "bf16"),
-        ("sparse16", "bf16"), ("sparse16", "fp8"), ("prefill", "bf16"), ("prefill", "fp8")]
+        ("sparse16", "bf16"), ("sparse16", "fp8"), ("prefill", "bf16"), ("prefill", "fp8"),
+        ("sparse_b1", "fp8"), ("sparse_b8", "bf16"), ("sparse_b64", "fp8"), ("sparse_b64", "bf16")]
 
 
 @pytest.mark.parametrize("name,dot", FULL)

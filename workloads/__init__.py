@@ -75,10 +75,20 @@ SPECS = {
     # query tokens of one sequence, each with its own top-2048 of the 16K keys
     "sparse_prefill": dict(batch=1, s_q=16384, h_q=16, d_rope=0, seq_len=16384, causal=False,
                            topk=2048, peaky=True, num_splits=0, dots=("bf16", "fp8")),
+    # the aiter PR's batch series (ROCm/aiter PR #6199, the bench commit: decode
+    # at 1, 8 and 64 sequences, 16 heads, context 8192, top-k 2048): one query
+    # token per sequence (a decode step), the same rope-free shard, random
+    # (not peaky) queries
+    "sparse_b1": dict(batch=1, s_q=1, h_q=16, d_rope=0, seq_len=8192, causal=False,
+                      topk=2048, peaky=False, num_splits=0, dots=("bf16", "fp8")),
+    "sparse_b8": dict(batch=8, s_q=1, h_q=16, d_rope=0, seq_len=8192, causal=False,
+                      topk=2048, peaky=False, num_splits=0, dots=("bf16", "fp8")),
+    "sparse_b64": dict(batch=64, s_q=1, h_q=16, d_rope=0, seq_len=8192, causal=False,
+                       topk=2048, peaky=False, num_splits=0, dots=("bf16", "fp8")),
 }
 
 SEEDS = {"tiny": 1, "mtp": 2, "varlen": 3, "large": 4, "sparse": 5, "metric": 6, "sparse16": 7, "prefill": 8,
-         "sparse_prefill": 9}
+         "sparse_prefill": 9, "sparse_b1": 10, "sparse_b8": 11, "sparse_b64": 12}
 
 
 @dataclass
