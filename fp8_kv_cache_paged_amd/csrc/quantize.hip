@@ -50,34 +50,39 @@ __device__ inline float block_max(float x, float* red) {
   return x;
 }
 
-// Partial amax of workgroup blockIdx.x: 16-byte chunks (8 bf16) of the nope
-// values of written tokens, grid-strided, four chunks per thread in flight.
-// The value and slot loads do not depend on each other (a chunk past the end
-// re-reads the last one and is masked), so both go out together.
+// Partial amax of workgroup blockIdx.x. A token's 512 nope values are one
+// wave-wide 16-byte load (lane l: values 8 l .. 8 l + 7); each wave takes
+// tokens grid-strided, eight in flight. The eight slots come first, as one
+// load (lane l reads the slot of token l % 8), and are read out lane by lane
+// once the value loads are in flight.
 __global__ __launch_bounds__(kQThreads) void kv_amax_kernel(const uint16_t* __restrict__ ckv,
                                                             const int32_t* __restrict__ slots,
                                                             int num_tokens, long cache_rows,
                                                             float* __restrict__ partials) {
+  constexpr int kInFlight = 8;
   __shared__ float red[4];
-  const long chunks = (long)num_tokens * 64;   // 512 values = 64 chunks per token
-  const long stride = (long)gridDim.x * kQThreads;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int waves = gridDim.x * (kQThreads / 64);
   float m = 0.f;
-  for (long c0 = (long)blockIdx.x * kQThreads + threadIdx.x; c0 < chunks; c0 += 4 * stride) {
-    q_i32x4 v[4];
-    int sl[4];
+  for (int t0 = blockIdx.x * (kQThreads / 64) + wave; t0 < num_tokens; t0 += kInFlight * waves) {
+    const int tl = t0 + (lane % kInFlight) * waves;
+    const int sl = slots[tl < num_tokens ? tl : num_tokens - 1];
+    q_i32x4 v[kInFlight];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long c = c0 + u * stride < chunks ? c0 + u * stride : chunks - 1;
-      v[u] = *reinterpret_cast<const q_i32x4*>(ckv + c * 8);
-      sl[u] = c0 + u * stride < chunks ? slots[c >> 6] : -1;
+    for (int u = 0; u < kInFlight; ++u) {
+      const int t = t0 + u * waves;
+      const int tc = t < num_tokens ? t : num_tokens - 1;   // past the end: re-read, masked
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const q_i32x4*>(ckv + (long)tc * 512) + lane);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kInFlight; ++u) {
       float mu = 0.f;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         mu = fmaxf(mu, fmaxf(fabsf(bf16_lo_f((unsigned)v[u][d])), fabsf(bf16_hi_f((unsigned)v[u][d]))));
-      m = slot_ok(sl[u], cache_rows) ? fmaxf(m, mu) : m;
+      const bool ok = t0 + u * waves < num_tokens && slot_ok(__builtin_amdgcn_readlane(sl, u), cache_rows);
+      m = ok ? fmaxf(m, mu) : m;
     }
   }
   m = block_max(m, red);
@@ -94,6 +99,24 @@ __device__ inline int enc4(float a, float b, float c, float d) {
 __device__ inline float qv(float x, float scale) {
   const float y = __fdiv_rn(x, scale);   // correctly rounded f32 division
   return fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
+}
+
+// The same code through the reciprocal: y = RN(1 / scale) (correctly
+// rounded, computed once), q0 = RN(x y) within an ulp or two of x / scale,
+// then two residual corrections q <- RN(q + (x - q scale) y) with the
+// residual exact under an fma. By Markstein's theorem (the correction of a
+// quotient within an ulp by the correctly rounded reciprocal gives the
+// correctly rounded quotient) the second step yields RN(x / scale), the
+// division above, for scales in [2^-100, 2^100] (no overflow of y, no
+// underflow of a residual that decides a code). The sign is taken from x (the
+// quotient's, a -0 input stays -0); a quotient past +-448, inf or NaN comes
+// from q0 and saturates as above.
+__device__ inline float qv_rcp(float x, float scale, float y) {
+  const float q0 = x * y;
+  const float q1 = fmaf(fmaf(-q0, scale, x), y, q0);
+  const float q2 = fmaf(fmaf(-q1, scale, x), y, q1);
+  const float q = fabsf(q0) <= kE4m3Max ? copysignf(q2, x) : q0;
+  return fminf(fmaxf(q, -kE4m3Max), kE4m3Max);
 }
 
 template <int ROPE>
@@ -127,30 +150,52 @@ __global__ __launch_bounds__(kQThreads) void kv_encode_kernel(const uint16_t* __
   }
   __syncthreads();
   const float scale = s_scale;
+  const float rcp = __fdiv_rn(1.f, scale);
+  const bool by_rcp = scale >= 0x1p-100f && scale <= 0x1p100f;   // uniform
 
+  // two chunks per thread per step, both loaded before either is encoded
   const long chunks = (long)num_tokens * CPR;
-  for (long c = (long)blockIdx.x * kQThreads + threadIdx.x; c < chunks; c += (long)gridDim.x * kQThreads) {
-    const long tok = c / CPR;
-    const int part = (int)(c - tok * CPR);
-    // the slot is only needed for the store: the value loads below do not
-    // wait for it
-    const int slot = slots[tok];
-    q_i32x4 o;
-    if (part < 32) {
-      // nope values 16 part .. +15 -> 16 code bytes
-      const q_i32x4* src = reinterpret_cast<const q_i32x4*>(ckv + tok * 512 + 16 * part);
-      const q_i32x4 a = src[0], b = src[1];
-      const unsigned w[8] = {(unsigned)a[0], (unsigned)a[1], (unsigned)a[2], (unsigned)a[3],
-                             (unsigned)b[0], (unsigned)b[1], (unsigned)b[2], (unsigned)b[3]};
+  const long stride = (long)gridDim.x * kQThreads;
+  for (long c0 = (long)blockIdx.x * kQThreads + threadIdx.x; c0 < chunks; c0 += 2 * stride) {
+    long tok[2];
+    int part[2], slot[2];
+    q_i32x4 a[2], b[2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o[k] = enc4(qv(bf16_lo_f(w[2 * k]), scale), qv(bf16_hi_f(w[2 * k]), scale),
-                    qv(bf16_lo_f(w[2 * k + 1]), scale), qv(bf16_hi_f(w[2 * k + 1]), scale));
-    } else {
-      // rope values 8 (part - 32) .. +7, copied
-      o = *reinterpret_cast<const q_i32x4*>(rope + tok * ROPE + 8 * (part - 32));
+    for (int u = 0; u < 2; ++u) {
+      const long c = c0 + u * stride < chunks ? c0 + u * stride : c0;   // past the end: chunk c0 again
+      tok[u] = c / CPR;
+      part[u] = (int)(c - tok[u] * CPR);
+      // the slot is only needed for the store: the value loads do not wait for it
+      slot[u] = c0 + u * stride < chunks ? slots[tok[u]] : -1;
+      if (part[u] < 32) {   // nope values 16 part .. +15
+        const q_i32x4* src = reinterpret_cast<const q_i32x4*>(ckv + tok[u] * 512 + 16 * part[u]);
+        a[u] = __builtin_nontemporal_load(src);
+        b[u] = __builtin_nontemporal_load(src + 1);
+      } else {              // rope values 8 (part - 32) .. +7, copied
+        a[u] = __builtin_nontemporal_load(reinterpret_cast<const q_i32x4*>(rope + tok[u] * ROPE + 8 * (part[u] - 32)));
+      }
     }
-    if (slot_ok(slot, cache_rows)) *reinterpret_cast<q_i32x4*>(kv + (long)slot * RB + 16 * part) = o;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      q_i32x4 o = a[u];
+      if (part[u] < 32) {   // 16 values -> 16 code bytes
+        const unsigned w[8] = {(unsigned)a[u][0], (unsigned)a[u][1], (unsigned)a[u][2], (unsigned)a[u][3],
+                               (unsigned)b[u][0], (unsigned)b[u][1], (unsigned)b[u][2], (unsigned)b[u][3]};
+        if (by_rcp) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            o[k] = enc4(qv_rcp(bf16_lo_f(w[2 * k]), scale, rcp), qv_rcp(bf16_hi_f(w[2 * k]), scale, rcp),
+                        qv_rcp(bf16_lo_f(w[2 * k + 1]), scale, rcp), qv_rcp(bf16_hi_f(w[2 * k + 1]), scale, rcp));
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            o[k] = enc4(qv(bf16_lo_f(w[2 * k]), scale), qv(bf16_hi_f(w[2 * k]), scale),
+                        qv(bf16_lo_f(w[2 * k + 1]), scale), qv(bf16_hi_f(w[2 * k + 1]), scale));
+        }
+      }
+      if (slot_ok(slot[u], cache_rows))
+        __builtin_nontemporal_store(o, reinterpret_cast<q_i32x4*>(kv + (long)slot[u] * RB + 16 * part[u]));
+    }
   }
 }
 

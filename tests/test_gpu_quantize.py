@@ -136,3 +136,35 @@ def test_quantized_cache_decodes_like_the_oracle():
     o = out.float().cpu().numpy()
     rel = np.linalg.norm(o - ref_o) / np.linalg.norm(ref_o)
     assert rel <= 5e-3 and np.abs(lse.cpu().numpy() - ref_l).max() <= 1e-3
+
+
+# Given scales for the every-value check: powers of two (every quotient exact,
+# ties of the e4m3fn grid included), inexact ones, a scale under which most
+# values saturate, and the ends of the range where the encoder changes from
+# the reciprocal form to the division (2^-100 and 2^100 take the reciprocal,
+# 1e-31 and 1e31 the division).
+EVERY_VALUE_SCALES = [2.0 ** -7, 1.0, 0.0071, 1.0 / 3.0, 1.7e-3, 3.0, 1e-30, 1e30,
+                      2.0 ** -100, 2.0 ** 100, 1e-31, 1e31, 0.013671875, 6.02e-5]
+
+
+@pytest.mark.parametrize("scale", EVERY_VALUE_SCALES)
+def test_quantize_every_bf16_value(scale):
+    """Every finite and infinite bf16 bit pattern (128 tokens of 512 values;
+    NaN patterns replaced by zero: the oracle gives them no code) encoded
+    under a given scale, byte for byte as the oracle's correctly rounded f32
+    division followed by saturation and round-to-nearest-even e4m3fn."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    nan = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x007F) != 0)
+    bits[nan] = 0
+    rng = np.random.default_rng(77)
+    ckv = bits[rng.permutation(65536)].reshape(128, 512)
+    rope = _bf16_bits(rng.standard_normal((128, 64)))
+    pages = 3
+    slots = rng.permutation(pages * 64)[:128].astype(np.int32)
+    kv = np.full((pages, 64, 1, 640), 0xFF, dtype=np.uint8)
+    sc = np.float32(scale)
+    ref, _ = cache.quantize_kv(ckv, rope, slots, kv, scale=sc)
+    got, ks, _ = _gpu(ckv, rope, slots, kv, scale=sc)
+    assert ks.view(np.uint32) == sc.view(np.uint32)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"scale {scale}: {len(bad)} bytes differ, first at {bad[:4].tolist()}"
