@@ -214,23 +214,37 @@ __global__ __launch_bounds__(kQThreads) void kv_encode_per_token_kernel(const ui
   const int lane = threadIdx.x & 63;
   const long tok = (long)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
   if (tok >= num_tokens) return;
+  // the value and rope loads go out with the slot's (all in bounds for any
+  // slot); a row that is not written is dropped once the slot is known
   const int slot = slots[tok];
-  if (!slot_ok(slot, cache_rows)) return;   // wave-uniform
   const q_i32x4 v = *reinterpret_cast<const q_i32x4*>(ckv + tok * 512 + 8 * lane);
+  q_i32x4 rv{};
+  if constexpr (ROPE > 0) {
+    if (lane < 8) rv = *reinterpret_cast<const q_i32x4*>(rope + tok * ROPE + 8 * lane);
+  }
+  if (!slot_ok(slot, cache_rows)) return;   // wave-uniform
   float m = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) m = fmaxf(m, fmaxf(fabsf(bf16_lo_f((unsigned)v[d])), fabsf(bf16_hi_f((unsigned)v[d]))));
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   const float scale = m > 0.f ? __fdiv_rn(m, kE4m3Max) : 1.f;
-  const int c0 = enc4(qv(bf16_lo_f((unsigned)v[0]), scale), qv(bf16_hi_f((unsigned)v[0]), scale),
-                      qv(bf16_lo_f((unsigned)v[1]), scale), qv(bf16_hi_f((unsigned)v[1]), scale));
-  const int c1 = enc4(qv(bf16_lo_f((unsigned)v[2]), scale), qv(bf16_hi_f((unsigned)v[2]), scale),
-                      qv(bf16_lo_f((unsigned)v[3]), scale), qv(bf16_hi_f((unsigned)v[3]), scale));
+  int c0, c1;
+  if (scale >= 0x1p-100f && scale <= 0x1p100f) {   // wave-uniform
+    const float rcp = __fdiv_rn(1.f, scale);
+    c0 = enc4(qv_rcp(bf16_lo_f((unsigned)v[0]), scale, rcp), qv_rcp(bf16_hi_f((unsigned)v[0]), scale, rcp),
+              qv_rcp(bf16_lo_f((unsigned)v[1]), scale, rcp), qv_rcp(bf16_hi_f((unsigned)v[1]), scale, rcp));
+    c1 = enc4(qv_rcp(bf16_lo_f((unsigned)v[2]), scale, rcp), qv_rcp(bf16_hi_f((unsigned)v[2]), scale, rcp),
+              qv_rcp(bf16_lo_f((unsigned)v[3]), scale, rcp), qv_rcp(bf16_hi_f((unsigned)v[3]), scale, rcp));
+  } else {
+    c0 = enc4(qv(bf16_lo_f((unsigned)v[0]), scale), qv(bf16_hi_f((unsigned)v[0]), scale),
+              qv(bf16_lo_f((unsigned)v[1]), scale), qv(bf16_hi_f((unsigned)v[1]), scale));
+    c1 = enc4(qv(bf16_lo_f((unsigned)v[2]), scale), qv(bf16_hi_f((unsigned)v[2]), scale),
+              qv(bf16_lo_f((unsigned)v[3]), scale), qv(bf16_hi_f((unsigned)v[3]), scale));
+  }
   uint8_t* row = kv + (long)slot * RB;
   *reinterpret_cast<uint2*>(row + 8 * lane) = uint2{(unsigned)c0, (unsigned)c1};
   if constexpr (ROPE > 0) {
-    if (lane < 8) *reinterpret_cast<q_i32x4*>(row + 512 + 16 * lane) =
-        *reinterpret_cast<const q_i32x4*>(rope + tok * ROPE + 8 * lane);
+    if (lane < 8) *reinterpret_cast<q_i32x4*>(row + 512 + 16 * lane) = rv;
   }
   if (lane == 0) {
     k_scale[slot] = scale;

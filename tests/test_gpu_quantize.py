@@ -168,3 +168,45 @@ def test_quantize_every_bf16_value(scale):
     assert ks.view(np.uint32) == sc.view(np.uint32)
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"scale {scale}: {len(bad)} bytes differ, first at {bad[:4].tolist()}"
+
+
+def test_quantize_per_token_every_bf16_value():
+    """Per-token scales over every finite bf16 value: the non-NaN patterns
+    sorted by magnitude and cut into rows of 512, each row then given half of
+    another, smaller row's values (so quotients span many binades below the
+    row's amax / scale = 448); rows whose amax makes the scale leave
+    [2^-100, 2^100] take the division form, the others the reciprocal form.
+    Cache bytes and per-row scales byte for byte as the oracle's."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    vals = bits[finite]
+    mag = np.abs(torch.from_numpy(vals.view(np.int16)).view(torch.bfloat16).float().numpy())
+    vals = vals[np.argsort(mag, kind="stable")]
+    n = len(vals) // 512
+    rows = vals[: n * 512].reshape(n, 512).copy()
+    rng = np.random.default_rng(78)
+    for r in range(1, n):
+        j = int(rng.integers(0, r))
+        take = rng.choice(512, size=256, replace=False)
+        rows[r, take] = rows[j, rng.choice(512, size=256, replace=False)]
+    rows = np.ascontiguousarray(rows[:, rng.permutation(512)])
+    rope = _bf16_bits(rng.standard_normal((n, 64)))
+    pages = (n + 63) // 64 + 1
+    slots = rng.permutation(pages * 64)[:n].astype(np.int32)
+    kv0 = np.full((pages, 64, 1, 640), 0xFF, dtype=np.uint8)
+    sc0 = np.zeros((pages, 64), dtype=np.float32)
+    ref_cache, ref_sc = cache.quantize_kv_per_token(rows, rope, slots, kv0, sc0)
+    dev = "cuda:0"
+    kv = torch.from_numpy(kv0).to(dev)
+    ks = torch.from_numpy(sc0).to(dev)
+    vs = torch.from_numpy(sc0).to(dev)
+    mla.quantize_kv(torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).to(dev),
+                    torch.from_numpy(rope.view(np.int16)).view(torch.bfloat16).to(dev),
+                    torch.from_numpy(slots).to(dev), kv, ks, vs, compute_scale="per_token")
+    torch.cuda.synchronize()
+    scales = ref_sc.reshape(-1)[slots]
+    assert (scales < 2.0 ** -100).any() and ((scales >= 2.0 ** -100) & (scales <= 2.0 ** 100)).any()
+    bad = np.argwhere(kv.cpu().numpy() != ref_cache)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:4].tolist()}"
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), ref_sc.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), ref_sc.view(np.uint32))
