@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kQThreads) void kv_amax_kernel(const uint16_t* __re
     for (int u = 0; u < kInFlight; ++u) {
       const int t = t0 + u * waves;
       const int tc = t < num_tokens ? t : num_tokens - 1;   // past the end: re-read, masked
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const q_i32x4*>(ckv + (long)tc * 512) + lane);
+      v[u] = reinterpret_cast<const q_i32x4*>(ckv + (long)tc * 512)[lane];   // cached: see the encode order
     }
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
@@ -156,7 +156,14 @@ __global__ __launch_bounds__(kQThreads) void kv_encode_kernel(const uint16_t* __
   // two chunks per thread per step, both loaded before either is encoded
   const long chunks = (long)num_tokens * CPR;
   const long stride = (long)gridDim.x * kQThreads;
-  for (long c0 = (long)blockIdx.x * kQThreads + threadIdx.x; c0 < chunks; c0 += 2 * stride) {
+  // Steps in reverse: the amax pass reads the tokens in rising order with
+  // ordinary (cached) loads, so the last of them may still sit in the
+  // memory-side cache when this pass starts, and are read again first
+  // (benchmark cache: 292 -> 271 us per call with the scale computed).
+  const long first = (long)blockIdx.x * kQThreads + threadIdx.x;
+  const long nsteps = first < chunks ? (chunks - 1 - first) / (2 * stride) + 1 : 0;
+  for (long k = nsteps - 1; k >= 0; --k) {
+    const long c0 = first + k * (2 * stride);
     long tok[2];
     int part[2], slot[2];
     q_i32x4 a[2], b[2];
